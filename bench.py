@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the AcceptMoE verify-block MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3_30b]
+
+A step is one whole verify block (router -> selection -> permute -> grouped
+SwiGLU over the unique active experts -> combine) on one seeded synthetic
+64-node draft tree, with every input already resident in HBM.  Steps rotate
+over 8 seeded blocks and 4 independently drawn layer weight sets so that no
+expert weights can be served from the 256 MB Infinity Cache; each rotation
+slot is captured once in a HIP graph and replayed.
+
+Prints one JSON line: microseconds per verify block (lower is better), the
+achieved HBM bandwidth on unique-expert weight bytes, the roofline of the
+dominant kernel (gate/up + SwiGLU projection: its device time is taken with
+HIP events recorded by the library on the launch stream around that stage,
+over a live timed region), and the CPU oracle timed on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="qwen3_30b")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--blocks", type=int, default=8)
+    ap.add_argument("--stage-steps", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
+    ap.add_argument("--flags", type=int, default=None, help="override shape flags (1 = natural)")
+    ap.add_argument("--fixed-budget", type=int, default=None)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the one-GPU hot path only: this build has no multi-GPU "
+              "path (no collectives, no sharding); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_speculative_decoding_gemm_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = W.CONFIGS[args.config]
+    over = {}
+    if args.flags is not None:
+        over["flags"] = args.flags
+    if args.fixed_budget is not None:
+        over["fixed_budget"] = args.fixed_budget
+    cfg = cfg.with_(**over)
+    DT = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3FN}
+    shape = M.make_shape(cfg.N, cfg.H, cfg.I, cfg.E, cfg.k, cfg.n_depth,
+                         act_dtype=DT[cfg.act], w_dtype=DT[cfg.w], min_set=cfg.min_set,
+                         fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute,
+                         flags=cfg.flags)
+
+    # ---------------------------------------------------------------- setup --
+    t0 = time.time()
+    blocks = [W.make_block(cfg, s) for s in range(args.blocks)]
+    dblocks = []
+    for b in blocks:
+        dblocks.append(dict(
+            x=b.x.to(dev), parent=torch.from_numpy(b.parent).to(dev),
+            depth=torch.from_numpy(b.depth).to(dev), commit=torch.from_numpy(b.commit).to(dev),
+            resident=None if b.resident is None else torch.from_numpy(b.resident).to(dev)))
+    w_router = blocks[0].w_router.to(dev)
+    b_router = None if blocks[0].b_router is None else blocks[0].b_router.to(dev)
+    layers = []
+    host_w = []
+    for li in range(args.layers):
+        ew = W.expert_weights(cfg, layer=li, device=dev)
+        wd = dict(w_router=w_router, b_router=b_router, w13=ew["w13"], w2=ew["w2"],
+                  s13=ew["s13"], s2=ew["s2"])
+        if cfg.shared:
+            sw = W.shared_weights(cfg, layer=li, device=dev)
+            wd.update(w13_shared=sw["w13"][0], w2_shared=sw["w2"][0],
+                      s13_shared=None if sw["s13"] is None else sw["s13"][0],
+                      s2_shared=None if sw["s2"] is None else sw["s2"][0])
+        layers.append(M.VerifyLayer(shape, wd, device=dev))
+        host_w.append(wd)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers x {cfg.E} experts, "
+        f"{args.blocks} blocks")
+
+    S = max(args.blocks, args.layers)
+    slots = [(s % args.blocks, s % args.layers) for s in range(S)]
+
+    def run_slot(s, stream=None):
+        bi, li = slots[s]
+        d = dblocks[bi]
+        return layers[li].run(d["x"], d["parent"], d["depth"], d["commit"],
+                              resident=d["resident"], stream=stream)
+
+    # per-slot selection statistics (deterministic per slot)
+    stats = []
+    y_eager = []
+    for s in range(S):
+        out = run_slot(s)
+        torch.cuda.synchronize()
+        st = M.decode_stats(out["stats"])
+        if st["err_flags"]:
+            raise RuntimeError(f"slot {s}: device error flags {st['err_flags']:#x}")
+        stats.append(st)
+        y_eager.append(out["y"].clone())
+    U = [st["n_active"] for st in stats]
+    ebytes = cfg.expert_bytes() + cfg.scale_bytes()
+    shared_bytes = ebytes if cfg.shared else 0
+    uniq_bytes = [u * ebytes for u in U]
+
+    # ------------------------------------------------------- graph capture --
+    graphs = []
+    if not args.eager:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for s in range(S):  # one eager pass on the capture stream first
+                run_slot(s)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for s in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_slot(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        # every replay must reproduce the eager result
+        for s in range(S):
+            graphs[s].replay()
+            torch.cuda.synchronize()
+            bi, li = slots[s]
+            if not torch.equal(layers[li].out["y"].view(torch.uint8), y_eager[s].view(torch.uint8)):
+                raise RuntimeError(f"graph replay of slot {s} differs from eager")
+
+    def step(i):
+        s = i % S
+        if graphs:
+            graphs[s].replay()
+        else:
+            run_slot(s)
+
+    # -------------------------------------------------------- timed region --
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    us_block = ms_per_step * 1e3
+    bytes_per_step = statistics.mean(uniq_bytes[i % S] for i in range(args.steps))
+    uniq_gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    log(f"timed {args.steps} steps: {us_block:.2f} us/block, unique-expert {uniq_gbps:.0f} GB/s "
+        f"(wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
+
+    # ----------------------------------------- per-stage device time (live) --
+    stage_names = {M.STAGE_SELECT: "select", M.STAGE_PERMUTE: "permute",
+                   M.STAGE_GATEUP: "gateup_swiglu", M.STAGE_DOWN: "down",
+                   M.STAGE_COMBINE: "combine"}
+    stage_us = {}
+    stage_samples = {}
+    n_st = max(S, args.stage_steps)
+    for stage, name in stage_names.items():
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_st)]
+        for a, b in evs:          # materialise the event handles
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(n_st):
+            a, b = evs[i]
+            M.acceptmoe_set_stage_timer(stage, a.cuda_event, b.cuda_event)
+            run_slot(i % S)
+        M.acceptmoe_set_stage_timer(M.STAGE_NONE, None, None)
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        stage_samples[name] = times
+        stage_us[name] = statistics.mean(times)
+    g_us = stage_samples["gateup_swiglu"]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w]
+    ab = {"f32": 4, "bf16": 2}[cfg.act]
+    hb = 4 if cfg.w == "f32" else 2
+    s13_bytes = (2 * (cfg.I // 128) * (cfg.H // 128) * 4) if cfg.w == "fp8" else 0
+    gate_bytes = [U[i % S] * (2 * cfg.I * cfg.H * wb + s13_bytes) + cfg.N * cfg.H * ab
+                  + cfg.N * cfg.k * cfg.I * hb for i in range(n_st)]
+    achieved = sum(gate_bytes) / (sum(g_us) * 1e-6) / 1e9
+    log("stages (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+
+    # ------------------------------------------------------- CPU baseline --
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, blocks, host_w, slots, args.cpu_seconds)
+
+    result = {
+        "metric": "us per MoE verify block (64-node tree) + HBM GB/s on unique-expert bytes",
+        "value": round(us_block, 3),
+        "unit": "us/block",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-weights/bf16", "f32": "f32"}[cfg.w]
+        if cfg.act == "bf16" or cfg.w == "f32" else cfg.w,
+        "data": "synthetic (seeded blocks and random-init expert weights of the layer shape)",
+        "config": {"workload": f"{cfg.name}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} "
+                               f"N={cfg.N}-node tree, {cfg.act} act / {cfg.w} experts",
+                   "layers_rotated": args.layers, "blocks_rotated": args.blocks,
+                   "launch": "eager" if args.eager else "hip-graph replay",
+                   "flags": cfg.flags, "fixed_budget": cfg.fixed_budget},
+        "throughput": {"blocks_per_s": round(1e6 / us_block, 1),
+                       "verify_nodes_per_s": round(cfg.N * 1e6 / us_block, 1),
+                       "unique_expert_GBps": round(uniq_gbps, 1),
+                       "unique_expert_frac_of_peak": round(uniq_gbps / HBM_PEAK_GBPS, 4)},
+        "selection": {"U_mean": statistics.mean(U), "U_by_block": U,
+                      "eligible_mean": statistics.mean(st["n_eligible"] for st in stats),
+                      "natural_union_mean": statistics.mean(st["n_natural_union"] for st in stats),
+                      "r_eff_mean": round(statistics.mean(st["r_eff"] for st in stats), 3),
+                      "expert_bytes": ebytes},
+        "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": {"kernel": "gateup_kernel (gate/up projections + SwiGLU)",
+                     "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(statistics.mean(g_us), 3),
+                     "algorithmic_bytes_per_launch": round(statistics.mean(gate_bytes))},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, blocks, host_w, slots, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    from oracle import fp8 as OF8
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+    except Exception:
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t_used, n_done, times = 0.0, 0, []
+    for s, (bi, li) in enumerate(slots):
+        b = blocks[bi]
+        wd = host_w[li]
+        # fetch this block's experts to host memory first (not oracle work)
+        sel = O.select(k=cfg.k, parent=b.parent, depth=b.depth, commit=b.commit,
+                       x=W.to_exact_f64(b.x), w_router=W.to_exact_f64(b.w_router),
+                       b_router=None if b.b_router is None else b.b_router.numpy(),
+                       resident=b.resident, min_set=cfg.min_set,
+                       fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute,
+                       flags=cfg.flags)
+        used = sorted(set(int(e) for e in sel["topk_idx"].reshape(-1)))
+        cache = {}
+        for e in used:
+            if cfg.w == "fp8":
+                q13 = wd["w13"][e].cpu().numpy()
+                s13 = wd["s13"][e].cpu().numpy()
+                cache[e] = (q13, s13, wd["w2"][e].cpu().numpy(), wd["s2"][e].cpu().numpy())
+            else:
+                w13 = W.to_exact_f64(wd["w13"][e])
+                cache[e] = (w13[0], w13[1], W.to_exact_f64(wd["w2"][e]))
+
+        def fn(e, cache=cache):
+            v = cache[e]
+            if cfg.w == "fp8":
+                return (OF8.dequant_blocks(v[0][0], v[1][0]), OF8.dequant_blocks(v[0][1], v[1][1]),
+                        OF8.dequant_blocks(v[2], v[3]))
+            return v
+        shared_fn = None
+        if cfg.shared:
+            if cfg.w == "fp8":
+                q = wd["w13_shared"].cpu().numpy(); sc = wd["s13_shared"].cpu().numpy()
+                q2 = wd["w2_shared"].cpu().numpy(); sc2 = wd["s2_shared"].cpu().numpy()
+                shared_fn = lambda: (OF8.dequant_blocks(q[0], sc[0]), OF8.dequant_blocks(q[1], sc[1]),
+                                     OF8.dequant_blocks(q2, sc2))
+            else:
+                a = W.to_exact_f64(wd["w13_shared"]); c2 = W.to_exact_f64(wd["w2_shared"])
+                shared_fn = lambda: (a[0], a[1], c2)
+        t0 = time.perf_counter()
+        O.verify_block(k=cfg.k, x=W.to_exact_f64(b.x), expert_fn=fn, parent=b.parent,
+                       depth=b.depth, commit=b.commit, w_router=W.to_exact_f64(b.w_router),
+                       b_router=None if b.b_router is None else b.b_router.numpy(),
+                       resident=b.resident, min_set=cfg.min_set, fixed_budget=cfg.fixed_budget,
+                       reroute_budget=cfg.reroute, flags=cfg.flags, shared_fn=shared_fn)
+        dt = time.perf_counter() - t0
+        times.append(dt)
+        t_used += dt
+        n_done += 1
+        log(f"cpu oracle block {s}: {dt * 1e3:.1f} ms")
+        if t_used >= seconds:
+            break
+    us = statistics.mean(times) * 1e6
+    return {"value": round(us, 1), "unit": "us/block", "cores": threads,
+            "host_cpus": cores, "kind": "oracle",
+            "sample": f"{n_done} block(s) of the {cfg.name} workload (seeded, rotating layers), "
+                      f"full layer: fp64 selection, permute, SwiGLU experts, combine; "
+                      f"expert weights pre-fetched to host memory"}
+
+
+if __name__ == "__main__":
+    main()

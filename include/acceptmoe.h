@@ -1,0 +1,261 @@
+/*
+ * acceptmoe.h -- C ABI of the AcceptMoE verify-block MoE layer for MI355X (gfx950).
+ *
+ * One MoE layer forward over one speculative-decoding verification block: a
+ * draft tree (or a forest of trees for batched verification) of N nodes.
+ * Sources, cited per entry point below:
+ *   [AcceptMoE news]     news article on AcceptMoE (Imperial College London /
+ *                        Tile-AI), sections 01-04
+ *   [AcceptMoE abstract] arXiv 2608.02989, English abstract
+ *   [MoE-SD blog]        "MoE 与推测解码：计算、通信和接受率的联合优化"
+ *                        (charlestar.github.io): the single-GPU MoE layer pipeline
+ *   [EcoSpec]            arXiv 2607.12696, Figure 1 (latency linear in active
+ *                        experts; 44.04 MB per FP8 DeepSeek-V3.1 expert)
+ *
+ * Conventions shared by every entry point
+ *   - Arrays are dense, row-major, and live in DEVICE memory unless a comment
+ *     says "host".  The caller owns every buffer; the library allocates no
+ *     memory and keeps no state between calls (it is reentrant).
+ *   - All work is enqueued on the caller's stream; nothing synchronises and
+ *     nothing reads device memory on the host, so every call may be captured
+ *     in a hipGraph.
+ *   - Return value: 0 on success or a negative ACCEPTMOE_E* code, decided on
+ *     the host before anything is enqueued (except ACCEPTMOE_EHIP, a failed
+ *     launch).  acceptmoe_last_error() gives a detail string for the calling
+ *     thread.  Problems only the device can see (a malformed tree, a depth
+ *     out of range, a bad commitment table, a non-finite logit) set bits in
+ *     acceptmoe_stats.err_flags; the other outputs are then unspecified but
+ *     every index the library writes stays in range.
+ *   - dtype pairs (activations, expert weights): (F32, F32), (BF16, BF16),
+ *     (BF16, FP8_E4M3FN).  FP8 weights come with one fp32 scale per 128 x 128
+ *     block of each [out, in] matrix: w = decode(q) * s.
+ *   - Limits: 1 <= N <= 4096, 1 <= k <= 16, k <= E <= 256, H and I multiples
+ *     of 64 (128 with FP8 weights), H, I <= 16384.
+ */
+#ifndef ACCEPTMOE_H
+#define ACCEPTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ACCEPTMOE_OK = 0,
+  ACCEPTMOE_EINVAL = -1,  /* a bad argument: NULL, out-of-range size, small workspace */
+  ACCEPTMOE_ENOTSUP = -2, /* an unsupported dtype pair or flag                        */
+  ACCEPTMOE_EHIP = -3     /* a kernel launch failed (hipGetLastError)                 */
+};
+
+typedef enum {
+  ACCEPTMOE_F32 = 0,
+  ACCEPTMOE_BF16 = 1,
+  ACCEPTMOE_FP8_E4M3FN = 2
+} acceptmoe_dtype;
+
+enum {
+  ACCEPTMOE_F_NATURAL = 1u << 0,   /* every expert eligible: natural routing (standard SD) */
+  ACCEPTMOE_F_NO_RENORM = 1u << 1, /* gates = raw softmax scores of the chosen experts     */
+  ACCEPTMOE_F_LOGITS_IN = 1u << 2  /* read logits_in instead of computing x W_r^T + b_r    */
+};
+
+/* bits of acceptmoe_stats.err_flags */
+enum {
+  ACCEPTMOE_ERR_BAD_TREE = 1u << 0,  /* parent not an earlier node, or depth != parent's + 1 */
+  ACCEPTMOE_ERR_DEPTH = 1u << 1,     /* depth outside [0, n_depth)                          */
+  ACCEPTMOE_ERR_NONFINITE = 1u << 2, /* a router logit is NaN or infinite                   */
+  ACCEPTMOE_ERR_COMMIT = 1u << 3     /* a commitment probability is negative or not finite  */
+};
+
+/* Problem description; passed by HOST pointer and read during the call. */
+typedef struct acceptmoe_shape {
+  int32_t N;              /* verify nodes (all trees of the block)                         */
+  int32_t H;              /* hidden size                                                   */
+  int32_t I;              /* expert intermediate size                                      */
+  int32_t E;              /* routed experts                                                */
+  int32_t k;              /* experts per node                                              */
+  int32_t n_depth;        /* entries of commit[]                                           */
+  int32_t min_set;        /* smallest eligible set; the floor is max(k, min_set)           */
+  int32_t fixed_budget;   /* 0: self-size (AcceptMoE); B > 0: set size B (AcceptMoE-B)     */
+  int32_t reroute_budget; /* R: most experts residency-aware pruning may drop              */
+  uint32_t flags;         /* ACCEPTMOE_F_*                                                 */
+  int32_t act_dtype;      /* acceptmoe_dtype of x, w_router and y                          */
+  int32_t w_dtype;        /* acceptmoe_dtype of the expert weights                         */
+} acceptmoe_shape;
+
+/* Per-block statistics, written by the device. */
+typedef struct acceptmoe_stats {
+  int32_t n_anchor;             /* |A|: experts in the roots' natural top-k               */
+  int32_t n_selfsize;           /* |S| after self-sizing, before pruning                  */
+  int32_t n_eligible;           /* |S| after pruning                                       */
+  int32_t n_pruned;             /* experts removed by residency-aware pruning              */
+  int32_t n_active;             /* U: unique experts of the restricted assignments         */
+  int32_t n_active_nonresident; /* of those, not resident (0 without a mask)               */
+  int32_t n_natural_union;      /* unique experts of the natural top-k assignments         */
+  int32_t err_flags;            /* ACCEPTMOE_ERR_* bits                                    */
+  double r_eff;                 /* effective rank exp(H(D / sum D)); 0 if sum D = 0        */
+  double demand_total;          /* sum of D                                               */
+} acceptmoe_stats;
+
+/* ---------------------------------------------------------------------------
+ * acceptmoe_select -- router, AcceptMoE eligibility, restricted top-k, gates.
+ *
+ * [MoE-SD blog, MoE layer]: logits l = x W_r^T + b_r; scores p = softmax(l)
+ *   over all E experts; each node's natural top-k by l (ties: lower index).
+ * [AcceptMoE news §02, abstract]: demand D_e = sum over nodes i of
+ *   commit[depth_i] * p_ie for e in node i's natural top-k; anchor A = union of
+ *   the roots' natural top-k; set size n = min(E, max(round-half-up(r_eff) or
+ *   fixed_budget, |A|, max(k, min_set))) with r_eff = exp(entropy of D/sum D);
+ *   S = A + the highest-demand others (ties: lower index).  With a resident
+ *   mask, non-resident non-anchor members of S are dropped in (demand
+ *   ascending, index descending) order, at most reroute_budget of them, never
+ *   below max(k, min_set).
+ * [AcceptMoE abstract]: each node's top-k is then taken over S only; gates
+ *   are the chosen scores renormalised to sum to one (F_NO_RENORM: raw).
+ *
+ *   x         [N,H] act_dtype        w_router [E,H] act_dtype
+ *   b_router  [E] fp32 or NULL       logits_in [N,E] fp32, used iff F_LOGITS_IN
+ *   parent    [N] int32: -1 for a root, else an earlier node index
+ *   depth     [N] int32: 0 for a root, parent's depth + 1 otherwise
+ *   commit    [n_depth] fp32: commitment probability per depth, >= 0
+ *   resident  [E] uint8 (nonzero = resident) or NULL: no pruning
+ *   logits_out [N,E] fp32 or NULL    eligible [E] uint8 (1 = in S)
+ *   topk_idx  [N,k] int32            topk_gate [N,k] fp32
+ *   stats     one acceptmoe_stats (device)
+ *   ws        workspace of at least acceptmoe_select_workspace_size(shape) bytes
+ * ------------------------------------------------------------------------- */
+size_t acceptmoe_select_workspace_size(const acceptmoe_shape* shape);
+int acceptmoe_select(const acceptmoe_shape* shape, const void* x, const void* w_router,
+                     const float* b_router, const float* logits_in, const int32_t* parent,
+                     const int32_t* depth, const float* commit, const uint8_t* resident,
+                     float* logits_out, uint8_t* eligible, int32_t* topk_idx, float* topk_gate,
+                     acceptmoe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_permute -- group the N*k assignments by expert.
+ *
+ * [MoE-SD blog, MoE layer]: assignment a = i*k + j goes to expert
+ * topk_idx[a]; counts[e] = assignments of e; offsets[E+1] = exclusive prefix
+ * sum of counts; sorted_assign[N*k] = assignment ids stably sorted by expert;
+ * inv_pos[sorted_assign[t]] = t; active[0..n_active) = experts with
+ * counts > 0, ascending (entries past n_active are left untouched).
+ * Every topk_idx entry must lie in [0, E) (an entry outside is clamped into
+ * range: no access leaves its buffer, the grouping is then unspecified).
+ * The result is deterministic.
+ * ------------------------------------------------------------------------- */
+int moe_route_permute(int32_t N, int32_t k, int32_t E, const int32_t* topk_idx, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_assign, int32_t* inv_pos,
+                      int32_t* active, int32_t* n_active, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu -- SwiGLU experts over the unique active experts only.
+ *
+ * [MoE-SD blog, MoE layer; EcoSpec Fig. 1]: for every active expert e and
+ * every row t in [offsets[e], offsets[e+1]), with token i = sorted_assign[t]/k:
+ *   y_perm[t,:] = (silu(x_i Wg_e^T) * (x_i Wu_e^T)) Wd_e^T
+ * Each active expert's weights are streamed from HBM once per group of at most
+ * 64 rows.  silu(z) = z / (1 + exp(-z)); the SwiGLU hidden is rounded to bf16
+ * before the down projection unless w_dtype is F32.
+ *
+ *   x   [N,H] act_dtype
+ *   w13 [E,2,I,H] w_dtype (gate rows, then up rows)   w2 [E,H,I] w_dtype
+ *   s13 [E,2,I/128,H/128] fp32, s2 [E,H/128,I/128] fp32: FP8 only, else NULL
+ *   offsets [E+1], sorted_assign [N*k], active [E], n_active [1]: as written
+ *     by moe_route_permute
+ *   y_perm [N*k,H] fp32 (rows of inactive experts are not written)
+ *   ws  at least moe_grouped_swiglu_workspace_size(N, k, I, w_dtype) bytes
+ * The shared expert of a layer is this call with E = 1, k = 1,
+ * offsets = {0, N}, sorted_assign = 0..N-1, active = {0}, n_active = {1}.
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace_size(int32_t N, int32_t k, int32_t I, int32_t w_dtype);
+int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
+                       int32_t act_dtype, int32_t w_dtype, const void* x, const void* w13,
+                       const void* w2, const float* s13, const float* s2,
+                       const int32_t* offsets, const int32_t* sorted_assign,
+                       const int32_t* active, const int32_t* n_active, float* y_perm,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine -- unpermute and gate-weighted sum.
+ *
+ * [MoE-SD blog, MoE layer]: y[i,:] = sum_j topk_gate[i,j] * y_perm[inv_pos[i*k+j],:]
+ * (+ y_shared[i,:], the always-on shared expert, unweighted), written in
+ * act_dtype (bf16: round to nearest even).
+ *   y_perm [N*k,H] fp32, inv_pos [N*k], topk_gate [N,k] fp32,
+ *   y_shared [N,H] fp32 or NULL, y [N,H] act_dtype
+ * ------------------------------------------------------------------------- */
+int moe_combine(int32_t N, int32_t k, int32_t H, int32_t act_dtype, const float* y_perm,
+                const int32_t* inv_pos, const float* topk_gate, const float* y_shared, void* y,
+                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * verify_block -- the whole layer for one verification block:
+ * acceptmoe_select -> moe_route_permute -> moe_grouped_swiglu (+ shared
+ * expert) -> moe_combine, enqueued back to back on one stream.
+ * ------------------------------------------------------------------------- */
+typedef struct acceptmoe_inputs {  /* device pointers, as in the calls above */
+  const void* x;
+  const void* w_router;
+  const float* b_router;     /* or NULL */
+  const float* logits_in;    /* used iff F_LOGITS_IN */
+  const int32_t* parent;
+  const int32_t* depth;
+  const float* commit;
+  const uint8_t* resident;   /* or NULL */
+  const void* w13;
+  const void* w2;
+  const float* s13;          /* FP8 only */
+  const float* s2;           /* FP8 only */
+  const void* w13_shared;    /* [2,I,H] or NULL: no shared expert */
+  const void* w2_shared;     /* [H,I] */
+  const float* s13_shared;   /* [2,I/128,H/128], FP8 only */
+  const float* s2_shared;    /* [H/128,I/128],   FP8 only */
+} acceptmoe_inputs;
+
+typedef struct acceptmoe_outputs { /* device pointers; only y is required */
+  void* y;                   /* [N,H] act_dtype */
+  float* logits_out;         /* [N,E] */
+  uint8_t* eligible;         /* [E] */
+  int32_t* topk_idx;         /* [N,k] */
+  float* topk_gate;          /* [N,k] */
+  int32_t* counts;           /* [E] */
+  int32_t* active;           /* [E] */
+  acceptmoe_stats* stats;    /* [1] */
+} acceptmoe_outputs;
+
+size_t acceptmoe_workspace_size(const acceptmoe_shape* shape);
+int verify_block(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
+                 const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Profiling aid: per-thread stage timer.  After
+ * acceptmoe_set_stage_timer(stage, start, stop), every later verify_block call
+ * on this host thread records `start` on its stream right before the first
+ * kernel of `stage` and `stop` right after its last kernel, so
+ * hipEventElapsedTime(start, stop) is that stage's device time.  stage = 0
+ * (or NULL events) turns it off.  The events belong to the caller.  Returns
+ * ACCEPTMOE_EINVAL for an unknown stage.
+ * ------------------------------------------------------------------------- */
+enum {
+  ACCEPTMOE_STAGE_NONE = 0,
+  ACCEPTMOE_STAGE_SELECT = 1,   /* router, per-node scores, set selection, restricted top-k */
+  ACCEPTMOE_STAGE_PERMUTE = 2,  /* group by expert                                          */
+  ACCEPTMOE_STAGE_GATEUP = 3,   /* routed experts: gate/up projections + SwiGLU             */
+  ACCEPTMOE_STAGE_DOWN = 4,     /* routed experts: down projection                          */
+  ACCEPTMOE_STAGE_EXPERTS = 5,  /* routed experts: both projections                         */
+  ACCEPTMOE_STAGE_COMBINE = 6   /* shared expert (if any) + unpermute/combine               */
+};
+int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop);
+
+/* Messages and version (host). */
+const char* acceptmoe_strerror(int code);
+const char* acceptmoe_last_error(void);
+const char* acceptmoe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ACCEPTMOE_H */

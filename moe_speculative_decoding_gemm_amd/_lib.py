@@ -1,0 +1,291 @@
+"""ctypes binding of libacceptmoe.so (the C ABI in include/acceptmoe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels.
+Tensors are PyTorch device tensors (torch provides memory and streams); each
+wrapper checks dtype, contiguity, device and shape, then passes raw pointers
+and the current stream.  The library must be built (``build()`` in
+``__graft_entry__`` or ``python moe_speculative_decoding_gemm_amd/build.py``);
+importing this module without it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import struct
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libacceptmoe.so")
+
+OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+F_NATURAL, F_NO_RENORM, F_LOGITS_IN = 1, 2, 4
+ERR_BAD_TREE, ERR_DEPTH, ERR_NONFINITE, ERR_COMMIT = 1, 2, 4, 8
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3FN,
+       torch.float8_e4m3fn: FP8_E4M3FN}
+
+
+class AcceptMoEError(RuntimeError):
+    def __init__(self, code: int, fn: str, detail: str):
+        super().__init__(f"{fn} failed ({code}): {detail}")
+        self.code = code
+
+
+class Shape(C.Structure):
+    _fields_ = [("N", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32),
+                ("k", C.c_int32), ("n_depth", C.c_int32), ("min_set", C.c_int32),
+                ("fixed_budget", C.c_int32), ("reroute_budget", C.c_int32),
+                ("flags", C.c_uint32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32)]
+
+
+class Inputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "x", "w_router", "b_router", "logits_in", "parent", "depth", "commit", "resident",
+        "w13", "w2", "s13", "s2", "w13_shared", "w2_shared", "s13_shared", "s2_shared")]
+
+
+class Outputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "y", "logits_out", "eligible", "topk_idx", "topk_gate", "counts", "active", "stats")]
+
+
+STATS_BYTES = 48
+_STATS_FIELDS = ("n_anchor", "n_selfsize", "n_eligible", "n_pruned", "n_active",
+                 "n_active_nonresident", "n_natural_union", "err_flags", "r_eff",
+                 "demand_total")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python moe_speculative_decoding_gemm_amd/build.py)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    sig = {
+        "acceptmoe_select_workspace_size": (sz, [vp]),
+        "acceptmoe_select": (C.c_int, [vp] + [vp] * 13 + [vp, sz, vp]),
+        "moe_route_permute": (C.c_int, [i32, i32, i32] + [vp] * 7 + [vp]),
+        "moe_grouped_swiglu_workspace_size": (sz, [i32, i32, i32, i32]),
+        "moe_grouped_swiglu": (C.c_int, [i32] * 7 + [vp] * 10 + [vp, sz, vp]),
+        "moe_combine": (C.c_int, [i32] * 4 + [vp] * 5 + [vp]),
+        "acceptmoe_workspace_size": (sz, [vp]),
+        "verify_block": (C.c_int, [vp, vp, vp, vp, sz, vp]),
+        "acceptmoe_set_stage_timer": (C.c_int, [i32, vp, vp]),
+        "acceptmoe_strerror": (C.c_char_p, [C.c_int]),
+        "acceptmoe_last_error": (C.c_char_p, []),
+        "acceptmoe_version": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
+            "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
+            "acceptmoe_workspace_size", "verify_block", "acceptmoe_set_stage_timer",
+            "acceptmoe_strerror",
+            "acceptmoe_last_error", "acceptmoe_version")
+
+
+def raw():
+    """The ctypes library object (for tests of the bare C ABI)."""
+    return _lib
+
+
+STAGE_NONE, STAGE_SELECT, STAGE_PERMUTE, STAGE_GATEUP, STAGE_DOWN, STAGE_EXPERTS, \
+    STAGE_COMBINE = range(7)
+
+
+def acceptmoe_set_stage_timer(stage: int, start_event, stop_event):
+    """start_event / stop_event: raw hipEvent_t handles (int) or None."""
+    _check(_lib.acceptmoe_set_stage_timer(stage, start_event, stop_event),
+           "acceptmoe_set_stage_timer")
+
+
+def version() -> str:
+    return _lib.acceptmoe_version().decode()
+
+
+def _check(rc: int, fn: str):
+    if rc != 0:
+        raise AcceptMoEError(rc, fn, _lib.acceptmoe_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, dev=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def dtype_code(t: torch.dtype) -> int:
+    return _DT[t]
+
+
+def make_shape(N, H, I, E, k, n_depth, act_dtype=BF16, w_dtype=BF16, min_set=0,
+               fixed_budget=0, reroute_budget=0, flags=0) -> Shape:
+    return Shape(N, H, I, E, k, n_depth, min_set, fixed_budget, reroute_budget, flags,
+                 act_dtype, w_dtype)
+
+
+def decode_stats(t: torch.Tensor) -> dict:
+    """acceptmoe_stats from a STATS_BYTES uint8 device (or host) tensor."""
+    b = bytes(t.detach().to("cpu").numpy().tobytes())
+    vals = struct.unpack("<8i2d", b[:STATS_BYTES])
+    return dict(zip(_STATS_FIELDS, vals))
+
+
+def new_stats(device=None) -> torch.Tensor:
+    return torch.zeros(STATS_BYTES, dtype=torch.uint8, device=device or "cuda")
+
+
+def _act_dt(shape: Shape):
+    return torch.float32 if shape.act_dtype == F32 else torch.bfloat16
+
+
+def _w_dt(shape: Shape):
+    return {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3FN: (torch.uint8, torch.float8_e4m3fn)}[shape.w_dtype]
+
+
+# ----------------------------------------------------------------- select --
+def acceptmoe_select_workspace_size(shape: Shape) -> int:
+    return int(_lib.acceptmoe_select_workspace_size(C.byref(shape)))
+
+
+def acceptmoe_select(shape: Shape, x, w_router, b_router, logits_in, parent, depth, commit,
+                     resident, logits_out, eligible, topk_idx, topk_gate, stats, ws,
+                     stream=None):
+    N, H, E, k = shape.N, shape.H, shape.E, shape.k
+    adt = _act_dt(shape)
+    args = [
+        _ptr(x, "x", adt, (N, H)), _ptr(w_router, "w_router", adt, (E, H)),
+        _ptr(b_router, "b_router", torch.float32, (E,)),
+        _ptr(logits_in, "logits_in", torch.float32, (N, E)),
+        _ptr(parent, "parent", torch.int32, (N,)), _ptr(depth, "depth", torch.int32, (N,)),
+        _ptr(commit, "commit", torch.float32, (shape.n_depth,)),
+        _ptr(resident, "resident", torch.uint8, (E,)),
+        _ptr(logits_out, "logits_out", torch.float32, (N, E)),
+        _ptr(eligible, "eligible", torch.uint8, (E,)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (N, k)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (N, k)),
+        _ptr(stats, "stats", torch.uint8, (STATS_BYTES,)),
+    ]
+    wsp = _ptr(ws, "ws", torch.uint8)
+    nb = ws.numel() if ws is not None else 0
+    _check(_lib.acceptmoe_select(C.byref(shape), *args, wsp, nb, _stream(stream)),
+           "acceptmoe_select")
+
+
+# ---------------------------------------------------------------- permute --
+def moe_route_permute(N, k, E, topk_idx, counts, offsets, sorted_assign, inv_pos, active,
+                      n_active, stream=None):
+    i32 = torch.int32
+    _check(_lib.moe_route_permute(
+        N, k, E, _ptr(topk_idx, "topk_idx", i32, (N, k)), _ptr(counts, "counts", i32, (E,)),
+        _ptr(offsets, "offsets", i32, (E + 1,)),
+        _ptr(sorted_assign, "sorted_assign", i32, (N * k,)),
+        _ptr(inv_pos, "inv_pos", i32, (N * k,)), _ptr(active, "active", i32, (E,)),
+        _ptr(n_active, "n_active", i32, (1,)), _stream(stream)), "moe_route_permute")
+
+
+# ---------------------------------------------------------------- experts --
+def moe_grouped_swiglu_workspace_size(N, k, I, w_dtype) -> int:
+    return int(_lib.moe_grouped_swiglu_workspace_size(N, k, I, w_dtype))
+
+
+def moe_grouped_swiglu(N, k, E, H, I, act_dtype, w_dtype, x, w13, w2, s13, s2, offsets,
+                       sorted_assign, active, n_active, y_perm, ws, stream=None):
+    adt = torch.float32 if act_dtype == F32 else torch.bfloat16
+    wdt = {F32: torch.float32, BF16: torch.bfloat16,
+           FP8_E4M3FN: (torch.uint8, torch.float8_e4m3fn)}[w_dtype]
+    i32 = torch.int32
+    fp8 = w_dtype == FP8_E4M3FN
+    _check(_lib.moe_grouped_swiglu(
+        N, k, E, H, I, act_dtype, w_dtype, _ptr(x, "x", adt, (N, H)),
+        _ptr(w13, "w13", wdt, (E, 2, I, H)), _ptr(w2, "w2", wdt, (E, H, I)),
+        _ptr(s13, "s13", torch.float32, (E, 2, I // 128, H // 128) if fp8 else None),
+        _ptr(s2, "s2", torch.float32, (E, H // 128, I // 128) if fp8 else None),
+        _ptr(offsets, "offsets", i32, (E + 1,)),
+        _ptr(sorted_assign, "sorted_assign", i32, (N * k,)),
+        _ptr(active, "active", i32, (E,)), _ptr(n_active, "n_active", i32, (1,)),
+        _ptr(y_perm, "y_perm", torch.float32, (N * k, H)), _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_swiglu")
+
+
+def moe_combine(N, k, H, act_dtype, y_perm, inv_pos, topk_gate, y_shared, y, stream=None):
+    adt = torch.float32 if act_dtype == F32 else torch.bfloat16
+    _check(_lib.moe_combine(
+        N, k, H, act_dtype, _ptr(y_perm, "y_perm", torch.float32, (N * k, H)),
+        _ptr(inv_pos, "inv_pos", torch.int32, (N * k,)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (N, k)),
+        _ptr(y_shared, "y_shared", torch.float32, (N, H)), _ptr(y, "y", adt, (N, H)),
+        _stream(stream)), "moe_combine")
+
+
+# ------------------------------------------------------------ whole block --
+def acceptmoe_workspace_size(shape: Shape) -> int:
+    return int(_lib.acceptmoe_workspace_size(C.byref(shape)))
+
+
+def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
+    """inputs/outputs: dicts keyed like acceptmoe_inputs / acceptmoe_outputs."""
+    N, H, I, E, k = shape.N, shape.H, shape.I, shape.E, shape.k
+    adt = _act_dt(shape)
+    wdt = _w_dt(shape)
+    fp8 = shape.w_dtype == FP8_E4M3FN
+    g = inputs.get
+    inp = Inputs(
+        _ptr(g("x"), "x", adt, (N, H)), _ptr(g("w_router"), "w_router", adt, (E, H)),
+        _ptr(g("b_router"), "b_router", torch.float32, (E,)),
+        _ptr(g("logits_in"), "logits_in", torch.float32, (N, E)),
+        _ptr(g("parent"), "parent", torch.int32, (N,)),
+        _ptr(g("depth"), "depth", torch.int32, (N,)),
+        _ptr(g("commit"), "commit", torch.float32, (shape.n_depth,)),
+        _ptr(g("resident"), "resident", torch.uint8, (E,)),
+        _ptr(g("w13"), "w13", wdt, (E, 2, I, H)), _ptr(g("w2"), "w2", wdt, (E, H, I)),
+        _ptr(g("s13"), "s13", torch.float32, (E, 2, I // 128, H // 128) if fp8 else None),
+        _ptr(g("s2"), "s2", torch.float32, (E, H // 128, I // 128) if fp8 else None),
+        _ptr(g("w13_shared"), "w13_shared", wdt, (2, I, H)),
+        _ptr(g("w2_shared"), "w2_shared", wdt, (H, I)),
+        _ptr(g("s13_shared"), "s13_shared", torch.float32, (2, I // 128, H // 128) if fp8 else None),
+        _ptr(g("s2_shared"), "s2_shared", torch.float32, (H // 128, I // 128) if fp8 else None))
+    o = outputs.get
+    out = Outputs(
+        _ptr(o("y"), "y", adt, (N, H)), _ptr(o("logits_out"), "logits_out", torch.float32, (N, E)),
+        _ptr(o("eligible"), "eligible", torch.uint8, (E,)),
+        _ptr(o("topk_idx"), "topk_idx", torch.int32, (N, k)),
+        _ptr(o("topk_gate"), "topk_gate", torch.float32, (N, k)),
+        _ptr(o("counts"), "counts", torch.int32, (E,)),
+        _ptr(o("active"), "active", torch.int32, (E,)),
+        _ptr(o("stats"), "stats", torch.uint8, (STATS_BYTES,)))
+    _check(_lib.verify_block(C.byref(shape), C.byref(inp), C.byref(out),
+                             _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0,
+                             _stream(stream)), "verify_block")

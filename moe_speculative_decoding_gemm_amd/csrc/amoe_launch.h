@@ -1,0 +1,82 @@
+// Host-side launchers of the AcceptMoE kernels (one per kernel family).
+// Called only by capi.cpp after it has validated every argument; each
+// launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace amoe {
+
+struct SelectArgs {
+  int N, H, E, k, n_depth, min_set, fixed_budget, reroute_budget;
+  uint32_t flags;
+  int act_bf16;  // 1: x and w_router are bf16, 0: fp32
+  const void* x;
+  const void* w_router;
+  const float* b_router;
+  const float* logits_in;
+  const int32_t* parent;
+  const int32_t* depth;
+  const float* commit;
+  const uint8_t* resident;
+  float* logits_out;  // may be null
+  uint8_t* eligible;
+  int32_t* topk_idx;
+  float* topk_gate;
+  void* stats;  // acceptmoe_stats*
+  // workspace carve-up
+  float* part;       // [ksplit][N][E] router partial sums
+  int ksplit;
+  int kslice;
+  float* logits;     // [N][E]
+  float* node_m;     // [N]
+  double* node_z;    // [N]
+  int32_t* nat;      // [N][k]
+  double* contrib;   // [N][E]
+  int32_t* node_err; // [N]
+};
+
+// router partial products, per-node softmax / natural top-k / demand terms,
+// set selection, restricted top-k and gates
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+void select_plan(int N, int H, int E, int num_cu, int* ksplit, int* kslice);
+
+// grouping of the N*k assignments by expert; resident/stats may be null
+hipError_t launch_permute(int N, int k, int E, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_assign, int32_t* inv_pos,
+                          int32_t* active, int32_t* n_active, const uint8_t* resident,
+                          void* stats, hipStream_t stream);
+
+// w_kind: 0 fp32, 1 bf16, 2 fp8 e4m3fn (+ scales); act_bf16 as above
+struct GroupedArgs {
+  int N, k, E, H, I;
+  int w_kind;
+  int act_bf16;
+  const void* x;
+  const void* w13;
+  const void* w2;
+  const float* s13;
+  const float* s2;
+  const int32_t* offsets;
+  const int32_t* sorted_assign;
+  const int32_t* active;
+  const int32_t* n_active;
+  float* y_perm;
+  void* h_perm;  // [N*k][I] bf16 (fp32 when w_kind == 0)
+  int num_cu;
+};
+// which: 0 both projections, 1 gate/up only, 2 down only
+hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);
+
+hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm,
+                          const int32_t* inv_pos, const float* topk_gate, const float* y_shared,
+                          void* y, hipStream_t stream);
+
+// identity grouping for the shared expert: offsets {0,N}, sorted_assign 0..N-1,
+// active {0}, n_active {1}
+hipError_t launch_shared_grouping(int N, int32_t* offsets, int32_t* sorted_assign,
+                                  int32_t* active, int32_t* n_active, hipStream_t stream);
+
+}  // namespace amoe

@@ -1,0 +1,487 @@
+// C ABI of the AcceptMoE verify-block MoE layer (see include/acceptmoe.h).
+// Host side only: argument checks, workspace carve-up, kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no device reads.
+
+#include "acceptmoe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "amoe_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// per-thread stage timer (acceptmoe_set_stage_timer)
+thread_local int g_timer_stage = 0;
+thread_local hipEvent_t g_timer_start = nullptr;
+thread_local hipEvent_t g_timer_stop = nullptr;
+
+void timer_mark(int stage, bool begin, hipStream_t stream) {
+  if (g_timer_stage != stage || !g_timer_start || !g_timer_stop) return;
+  (void)hipEventRecord(begin ? g_timer_start : g_timer_stop, stream);
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cu[kMaxDevices];
+
+// compute units of the current device (queried once per device)
+int num_cu() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_num_cu[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_num_cu[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+bool dtype_pair_ok(int act, int w) {
+  return (act == ACCEPTMOE_F32 && w == ACCEPTMOE_F32) ||
+         (act == ACCEPTMOE_BF16 && w == ACCEPTMOE_BF16) ||
+         (act == ACCEPTMOE_BF16 && w == ACCEPTMOE_FP8_E4M3FN);
+}
+
+int check_sizes(int N, int k, int E, int H, int I, int w_dtype, bool need_h, bool need_i) {
+  if (N < 1 || N > 4096) return fail(ACCEPTMOE_EINVAL, "N=%d outside [1, 4096]", N);
+  if (k < 1 || k > 16) return fail(ACCEPTMOE_EINVAL, "k=%d outside [1, 16]", k);
+  if (E < k || E > 256) return fail(ACCEPTMOE_EINVAL, "E=%d outside [k=%d, 256]", E, k);
+  const int mult = w_dtype == ACCEPTMOE_FP8_E4M3FN ? 128 : 64;
+  if (need_h && (H < mult || H > 16384 || H % mult))
+    return fail(ACCEPTMOE_EINVAL, "H=%d must be a multiple of %d in [%d, 16384]", H, mult, mult);
+  if (need_i && (I < mult || I > 16384 || I % mult))
+    return fail(ACCEPTMOE_EINVAL, "I=%d must be a multiple of %d in [%d, 16384]", I, mult, mult);
+  return ACCEPTMOE_OK;
+}
+
+int check_shape(const acceptmoe_shape* s, bool need_i) {
+  if (!s) return fail(ACCEPTMOE_EINVAL, "shape is NULL");
+  if (!dtype_pair_ok(s->act_dtype, s->w_dtype))
+    return fail(ACCEPTMOE_ENOTSUP, "unsupported dtype pair (act %d, weights %d)", s->act_dtype,
+                s->w_dtype);
+  if (s->flags & ~7u) return fail(ACCEPTMOE_ENOTSUP, "unknown flag bits %#x", s->flags);
+  int rc = check_sizes(s->N, s->k, s->E, s->H, s->I, s->w_dtype, true, need_i);
+  if (rc) return rc;
+  if (s->n_depth < 1) return fail(ACCEPTMOE_EINVAL, "n_depth=%d < 1", s->n_depth);
+  if (s->min_set < 0 || s->min_set > s->E)
+    return fail(ACCEPTMOE_EINVAL, "min_set=%d outside [0, E]", s->min_set);
+  if (s->fixed_budget < 0 || s->fixed_budget > s->E)
+    return fail(ACCEPTMOE_EINVAL, "fixed_budget=%d outside [0, E]", s->fixed_budget);
+  if (s->reroute_budget < 0) return fail(ACCEPTMOE_EINVAL, "reroute_budget < 0");
+  return ACCEPTMOE_OK;
+}
+
+// workspace of the selection stage, carved in a fixed order
+struct SelectWs {
+  float* part;
+  float* logits;
+  float* node_m;
+  double* node_z;
+  int32_t* nat;
+  double* contrib;
+  int32_t* node_err;
+  int ksplit, kslice;
+};
+
+SelectWs carve_select(Carver& c, const acceptmoe_shape* s) {
+  SelectWs w;
+  amoe::select_plan(s->N, s->H, s->E, 0, &w.ksplit, &w.kslice);
+  const size_t NE = static_cast<size_t>(s->N) * s->E;
+  w.part = c.take<float>(static_cast<size_t>(w.ksplit) * NE);
+  w.logits = c.take<float>(NE);
+  w.node_m = c.take<float>(s->N);
+  w.node_z = c.take<double>(s->N);
+  w.nat = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
+  w.contrib = c.take<double>(NE);
+  w.node_err = c.take<int32_t>(s->N);
+  return w;
+}
+
+size_t hidden_elem_bytes(int w_dtype) { return w_dtype == ACCEPTMOE_F32 ? 4 : 2; }
+
+struct VerifyWs {
+  SelectWs sel;
+  uint8_t* eligible;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_assign;
+  int32_t* inv_pos;
+  int32_t* active;
+  int32_t* n_active;
+  acceptmoe_stats* stats;
+  void* h_perm;
+  float* y_perm;
+  int32_t* sh_offsets;
+  int32_t* sh_sorted;
+  int32_t* sh_active;
+  int32_t* sh_n_active;
+  void* sh_h;
+  float* sh_y;
+};
+
+VerifyWs carve_verify(Carver& c, const acceptmoe_shape* s, bool shared) {
+  VerifyWs w;
+  w.sel = carve_select(c, s);
+  const size_t NK = static_cast<size_t>(s->N) * s->k;
+  w.eligible = c.take<uint8_t>(s->E);
+  w.topk_idx = c.take<int32_t>(NK);
+  w.topk_gate = c.take<float>(NK);
+  w.counts = c.take<int32_t>(s->E);
+  w.offsets = c.take<int32_t>(s->E + 1);
+  w.sorted_assign = c.take<int32_t>(NK);
+  w.inv_pos = c.take<int32_t>(NK);
+  w.active = c.take<int32_t>(s->E);
+  w.n_active = c.take<int32_t>(1);
+  w.stats = c.take<acceptmoe_stats>(1);
+  w.h_perm = c.take<char>(NK * s->I * hidden_elem_bytes(s->w_dtype));
+  w.y_perm = c.take<float>(NK * s->H);
+  w.sh_offsets = w.sh_sorted = w.sh_active = w.sh_n_active = nullptr;
+  w.sh_h = nullptr;
+  w.sh_y = nullptr;
+  if (shared) {
+    w.sh_offsets = c.take<int32_t>(2);
+    w.sh_sorted = c.take<int32_t>(s->N);
+    w.sh_active = c.take<int32_t>(1);
+    w.sh_n_active = c.take<int32_t>(1);
+    w.sh_h = c.take<char>(static_cast<size_t>(s->N) * s->I * hidden_elem_bytes(s->w_dtype));
+    w.sh_y = c.take<float>(static_cast<size_t>(s->N) * s->H);
+  }
+  return w;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(ACCEPTMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ACCEPTMOE_OK;
+}
+
+amoe::SelectArgs select_args(const acceptmoe_shape* s, const SelectWs& w) {
+  amoe::SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.N = s->N;
+  a.H = s->H;
+  a.E = s->E;
+  a.k = s->k;
+  a.n_depth = s->n_depth;
+  a.min_set = s->min_set;
+  a.fixed_budget = s->fixed_budget;
+  a.reroute_budget = s->reroute_budget;
+  a.flags = s->flags;
+  a.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
+  a.part = w.part;
+  a.ksplit = w.ksplit;
+  a.kslice = w.kslice;
+  a.logits = w.logits;
+  a.node_m = w.node_m;
+  a.node_z = w.node_z;
+  a.nat = w.nat;
+  a.contrib = w.contrib;
+  a.node_err = w.node_err;
+  return a;
+}
+
+int w_kind(int w_dtype) {
+  return w_dtype == ACCEPTMOE_F32 ? 0 : (w_dtype == ACCEPTMOE_BF16 ? 1 : 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* acceptmoe_version(void) { return "acceptmoe-mi355x 0.1 (gfx950)"; }
+
+const char* acceptmoe_last_error(void) { return g_err; }
+
+const char* acceptmoe_strerror(int code) {
+  switch (code) {
+    case ACCEPTMOE_OK:
+      return "success";
+    case ACCEPTMOE_EINVAL:
+      return "invalid argument";
+    case ACCEPTMOE_ENOTSUP:
+      return "unsupported dtype or flag";
+    case ACCEPTMOE_EHIP:
+      return "HIP launch failure";
+    default:
+      return "unknown error";
+  }
+}
+
+int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop) {
+  if (stage < ACCEPTMOE_STAGE_NONE || stage > ACCEPTMOE_STAGE_COMBINE)
+    return fail(ACCEPTMOE_EINVAL, "unknown stage %d", stage);
+  g_timer_stage = (start && stop) ? stage : 0;
+  g_timer_start = start;
+  g_timer_stop = stop;
+  return ACCEPTMOE_OK;
+}
+
+size_t acceptmoe_select_workspace_size(const acceptmoe_shape* s) {
+  if (check_shape(s, false)) return 0;
+  Carver c(nullptr);
+  carve_select(c, s);
+  return c.used;
+}
+
+int acceptmoe_select(const acceptmoe_shape* s, const void* x, const void* w_router,
+                     const float* b_router, const float* logits_in, const int32_t* parent,
+                     const int32_t* depth, const float* commit, const uint8_t* resident,
+                     float* logits_out, uint8_t* eligible, int32_t* topk_idx, float* topk_gate,
+                     acceptmoe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s, false);
+  if (rc) return rc;
+  const bool lin = (s->flags & ACCEPTMOE_F_LOGITS_IN) != 0;
+  if (lin ? !logits_in : (!x || !w_router))
+    return fail(ACCEPTMOE_EINVAL, lin ? "logits_in is NULL" : "x or w_router is NULL");
+  if (!parent || !depth || !commit || !eligible || !topk_idx || !topk_gate || !stats || !ws)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  const size_t need = acceptmoe_select_workspace_size(s);
+  if (ws_bytes < need)
+    return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
+  Carver c(ws);
+  const SelectWs w = carve_select(c, s);
+  amoe::SelectArgs a = select_args(s, w);
+  a.x = x;
+  a.w_router = w_router;
+  a.b_router = b_router;
+  a.logits_in = logits_in;
+  a.parent = parent;
+  a.depth = depth;
+  a.commit = commit;
+  a.resident = resident;
+  a.logits_out = logits_out;
+  a.eligible = eligible;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.stats = stats;
+  return hip_status(amoe::launch_select(a, stream), "acceptmoe_select");
+}
+
+int moe_route_permute(int32_t N, int32_t k, int32_t E, const int32_t* topk_idx, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_assign, int32_t* inv_pos,
+                      int32_t* active, int32_t* n_active, hipStream_t stream) {
+  int rc = check_sizes(N, k, E, 0, 0, ACCEPTMOE_F32, false, false);
+  if (rc) return rc;
+  if (!topk_idx || !counts || !offsets || !sorted_assign || !inv_pos || !active || !n_active)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  return hip_status(amoe::launch_permute(N, k, E, topk_idx, counts, offsets, sorted_assign,
+                                         inv_pos, active, n_active, nullptr, nullptr, stream),
+                    "moe_route_permute");
+}
+
+size_t moe_grouped_swiglu_workspace_size(int32_t N, int32_t k, int32_t I, int32_t w_dtype) {
+  if (N < 1 || k < 1 || I < 1) return 0;
+  return align256(static_cast<size_t>(N) * k * I * hidden_elem_bytes(w_dtype));
+}
+
+int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
+                       int32_t act_dtype, int32_t w_dtype, const void* x, const void* w13,
+                       const void* w2, const float* s13, const float* s2,
+                       const int32_t* offsets, const int32_t* sorted_assign,
+                       const int32_t* active, const int32_t* n_active, float* y_perm,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_pair_ok(act_dtype, w_dtype))
+    return fail(ACCEPTMOE_ENOTSUP, "unsupported dtype pair (act %d, weights %d)", act_dtype,
+                w_dtype);
+  // the shared expert is a call with E = 1, k = 1
+  if (N < 1 || N > 4096) return fail(ACCEPTMOE_EINVAL, "N=%d outside [1, 4096]", N);
+  if (k < 1 || k > 16 || E < 1 || E > 256)
+    return fail(ACCEPTMOE_EINVAL, "k=%d or E=%d out of range", k, E);
+  int rc = check_sizes(N, 1, 256, H, I, w_dtype, true, true);
+  if (rc) return rc;
+  if (!x || !w13 || !w2 || !offsets || !sorted_assign || !active || !n_active || !y_perm || !ws)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  if (w_dtype == ACCEPTMOE_FP8_E4M3FN && (!s13 || !s2))
+    return fail(ACCEPTMOE_EINVAL, "FP8 weights need s13 and s2");
+  const size_t need = moe_grouped_swiglu_workspace_size(N, k, I, w_dtype);
+  if (ws_bytes < need)
+    return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
+  amoe::GroupedArgs a;
+  a.N = N;
+  a.k = k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.w_kind = w_kind(w_dtype);
+  a.act_bf16 = act_dtype == ACCEPTMOE_BF16;
+  a.x = x;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.s13 = s13;
+  a.s2 = s2;
+  a.offsets = offsets;
+  a.sorted_assign = sorted_assign;
+  a.active = active;
+  a.n_active = n_active;
+  a.y_perm = y_perm;
+  a.h_perm = ws;
+  a.num_cu = num_cu();
+  return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
+}
+
+int moe_combine(int32_t N, int32_t k, int32_t H, int32_t act_dtype, const float* y_perm,
+                const int32_t* inv_pos, const float* topk_gate, const float* y_shared, void* y,
+                hipStream_t stream) {
+  if (act_dtype != ACCEPTMOE_F32 && act_dtype != ACCEPTMOE_BF16)
+    return fail(ACCEPTMOE_ENOTSUP, "unsupported activation dtype %d", act_dtype);
+  if (N < 1 || N > 4096 || k < 1 || k > 16 || H < 64 || H > 16384 || H % 64)
+    return fail(ACCEPTMOE_EINVAL, "bad sizes N=%d k=%d H=%d", N, k, H);
+  if (!y_perm || !inv_pos || !topk_gate || !y)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  return hip_status(amoe::launch_combine(N, k, H, act_dtype == ACCEPTMOE_BF16, y_perm, inv_pos,
+                                         topk_gate, y_shared, y, stream),
+                    "moe_combine");
+}
+
+size_t acceptmoe_workspace_size(const acceptmoe_shape* s) {
+  if (check_shape(s, true)) return 0;
+  Carver c(nullptr);
+  carve_verify(c, s, true);
+  return c.used;
+}
+
+int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                 const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc) return rc;
+  if (!in || !out) return fail(ACCEPTMOE_EINVAL, "inputs or outputs is NULL");
+  const bool lin = (s->flags & ACCEPTMOE_F_LOGITS_IN) != 0;
+  if (lin ? !in->logits_in : (!in->x || !in->w_router))
+    return fail(ACCEPTMOE_EINVAL, lin ? "logits_in is NULL" : "x or w_router is NULL");
+  if (!in->x || !in->parent || !in->depth || !in->commit || !in->w13 || !in->w2 || !out->y || !ws)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  const bool fp8 = s->w_dtype == ACCEPTMOE_FP8_E4M3FN;
+  if (fp8 && (!in->s13 || !in->s2)) return fail(ACCEPTMOE_EINVAL, "FP8 weights need s13 and s2");
+  const bool shared = in->w13_shared != nullptr;
+  if (shared && (!in->w2_shared || (fp8 && (!in->s13_shared || !in->s2_shared))))
+    return fail(ACCEPTMOE_EINVAL, "incomplete shared-expert weights");
+  const size_t need = acceptmoe_workspace_size(s);
+  if (ws_bytes < need)
+    return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
+
+  Carver c(ws);
+  const VerifyWs w = carve_verify(c, s, shared);
+  uint8_t* eligible = out->eligible ? out->eligible : w.eligible;
+  int32_t* topk_idx = out->topk_idx ? out->topk_idx : w.topk_idx;
+  float* topk_gate = out->topk_gate ? out->topk_gate : w.topk_gate;
+  int32_t* counts = out->counts ? out->counts : w.counts;
+  int32_t* active = out->active ? out->active : w.active;
+  acceptmoe_stats* stats = out->stats ? out->stats : w.stats;
+
+  amoe::SelectArgs a = select_args(s, w.sel);
+  a.x = in->x;
+  a.w_router = in->w_router;
+  a.b_router = in->b_router;
+  a.logits_in = in->logits_in;
+  a.parent = in->parent;
+  a.depth = in->depth;
+  a.commit = in->commit;
+  a.resident = in->resident;
+  a.logits_out = out->logits_out;
+  a.eligible = eligible;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.stats = stats;
+  timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
+  rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
+  timer_mark(ACCEPTMOE_STAGE_PERMUTE, true, stream);
+  rc = hip_status(amoe::launch_permute(s->N, s->k, s->E, topk_idx, counts, w.offsets,
+                                       w.sorted_assign, w.inv_pos, active, w.n_active,
+                                       in->resident, stats, stream),
+                  "verify_block/permute");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_PERMUTE, false, stream);
+  amoe::GroupedArgs g;
+  g.N = s->N;
+  g.k = s->k;
+  g.E = s->E;
+  g.H = s->H;
+  g.I = s->I;
+  g.w_kind = w_kind(s->w_dtype);
+  g.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
+  g.x = in->x;
+  g.w13 = in->w13;
+  g.w2 = in->w2;
+  g.s13 = in->s13;
+  g.s2 = in->s2;
+  g.offsets = w.offsets;
+  g.sorted_assign = w.sorted_assign;
+  g.active = active;
+  g.n_active = w.n_active;
+  g.y_perm = w.y_perm;
+  g.h_perm = w.h_perm;
+  g.num_cu = num_cu();
+  timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
+  timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
+  rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
+  timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
+  rc = hip_status(amoe::launch_grouped(g, stream, 2), "verify_block/experts down");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
+  timer_mark(ACCEPTMOE_STAGE_EXPERTS, false, stream);
+  timer_mark(ACCEPTMOE_STAGE_COMBINE, true, stream);
+  if (shared) {
+    rc = hip_status(amoe::launch_shared_grouping(s->N, w.sh_offsets, w.sh_sorted, w.sh_active,
+                                                 w.sh_n_active, stream),
+                    "verify_block/shared grouping");
+    if (rc) return rc;
+    amoe::GroupedArgs gs = g;
+    gs.k = 1;
+    gs.E = 1;
+    gs.w13 = in->w13_shared;
+    gs.w2 = in->w2_shared;
+    gs.s13 = in->s13_shared;
+    gs.s2 = in->s2_shared;
+    gs.offsets = w.sh_offsets;
+    gs.sorted_assign = w.sh_sorted;
+    gs.active = w.sh_active;
+    gs.n_active = w.sh_n_active;
+    gs.y_perm = w.sh_y;
+    gs.h_perm = w.sh_h;
+    rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
+    if (rc) return rc;
+  }
+  rc = hip_status(amoe::launch_combine(s->N, s->k, s->H, s->act_dtype == ACCEPTMOE_BF16,
+                                       w.y_perm, w.inv_pos, topk_gate,
+                                       shared ? w.sh_y : nullptr, out->y, stream),
+                  "verify_block/combine");
+  timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+"""A verify-block MoE layer bound to device weights: owns its workspace and
+output buffers (allocated once through torch) and calls ``verify_block``."""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+class VerifyLayer:
+    """One MoE layer's weights plus reusable buffers for ``verify_block``.
+
+    weights: dict with w_router [E,H], b_router [E] or None, w13 [E,2,I,H],
+    w2 [E,H,I], optional s13/s2 (FP8), optional w13_shared/w2_shared
+    (+ s13_shared/s2_shared).  All device tensors.
+    """
+
+    def __init__(self, shape: L.Shape, weights: dict, device=None, debug_outputs: bool = True):
+        self.shape = shape
+        self.w = dict(weights)
+        dev = torch.device(device or weights["w13"].device)
+        self.device = dev
+        N, H, E, k = shape.N, shape.H, shape.E, shape.k
+        adt = torch.float32 if shape.act_dtype == L.F32 else torch.bfloat16
+        nbytes = L.acceptmoe_workspace_size(shape)
+        if nbytes == 0:
+            raise L.AcceptMoEError(L.EINVAL, "acceptmoe_workspace_size",
+                                   L.raw().acceptmoe_last_error().decode())
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.out = {"y": torch.empty((N, H), dtype=adt, device=dev)}
+        if debug_outputs:
+            self.out.update(
+                logits_out=torch.empty((N, E), dtype=torch.float32, device=dev),
+                eligible=torch.empty(E, dtype=torch.uint8, device=dev),
+                topk_idx=torch.empty((N, k), dtype=torch.int32, device=dev),
+                topk_gate=torch.empty((N, k), dtype=torch.float32, device=dev),
+                counts=torch.empty(E, dtype=torch.int32, device=dev),
+                active=torch.empty(E, dtype=torch.int32, device=dev),
+                stats=torch.zeros(L.STATS_BYTES, dtype=torch.uint8, device=dev))
+
+    def run(self, x, parent, depth, commit, resident: Optional[torch.Tensor] = None,
+            logits_in: Optional[torch.Tensor] = None, stream=None) -> dict:
+        inputs = dict(self.w)
+        inputs.update(x=x, parent=parent, depth=depth, commit=commit, resident=resident,
+                      logits_in=logits_in)
+        L.verify_block(self.shape, inputs, self.out, self.ws, stream=stream)
+        return self.out

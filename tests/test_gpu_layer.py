@@ -1,0 +1,180 @@
+"""GPU parity of the whole layer (verify_block) and of the separate entry
+points against the oracle.
+
+Selection is made identical by handing the GPU's fp32 logits to the oracle
+(the logits themselves are checked within 1e-4 * max|l_ref|); the layer
+output y must then be within tol * max|y_ref| of the oracle's fp64 layer:
+tol = 1e-4 for fp32, 2e-2 for bf16, 6e-2 for fp8 weights.  Small shapes span
+several tiles with ragged tails; the full workload shapes are checked on all
+tokens (tiny, Qwen3-30B-shaped) or on sampled tokens from the per-token
+definition of the layer (the larger ones).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_cases import (TOL, check_selection, expert_fn_from, make_weights, max_rel_err,
+                       oracle_select, say, shape_of, shared_fn_from, upload_block)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer(lib, cfg, b, w, flags=None):
+    d = upload_block(b)
+    sh = shape_of(lib, cfg)
+    if flags is not None:
+        sh.flags = flags
+    weights = dict(w_router=d["w_router"], b_router=d["b_router"], **w)
+    layer = lib.VerifyLayer(sh, weights)
+    out = layer.run(d["x"], d["parent"], d["depth"], d["commit"], resident=d["resident"])
+    torch.cuda.synchronize()
+    return {k: v.clone() for k, v in out.items()}, lib.decode_stats(out["stats"])
+
+
+def oracle_layer(cfg, b, w, logits):
+    return O.verify_block(
+        k=cfg.k, x=W.to_exact_f64(b.x), expert_fn=expert_fn_from(cfg, w), parent=b.parent,
+        depth=b.depth, commit=b.commit, logits_in=logits, resident=b.resident,
+        min_set=cfg.min_set, fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute,
+        flags=cfg.flags, shared_fn=shared_fn_from(cfg, w))
+
+
+SMALL = [
+    # fp32 weights: the tiny layer and a ragged multi-tile variant
+    ("tiny", {}),
+    ("tiny", dict(E=12, k=3, H=192, I=320, N=23, tree="eagle", eagle_steps=3, eagle_width=4)),
+    # bf16: ragged token groups, I and H not multiples of 128
+    ("qwen3_30b", dict(E=24, k=4, H=320, I=192, N=37)),
+    ("gptoss_120b", dict(E=20, k=4, H=448, I=448, N=53, resident_slots=9, reroute=3)),
+    ("qwen3_235b_b025", dict(E=32, k=8, H=256, I=384, N=64)),
+    # fp8 weights with block scales and the shared expert; chains of 8
+    ("dsv31", dict(E=20, k=3, H=384, I=256, N=40, n_chains=5, chain_len=8)),
+    ("dsv31", dict(E=48, k=8, H=256, I=512, N=96, n_chains=12, chain_len=8)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL)
+def test_layer_parity_small(lib, name, over):
+    cfg = W.CONFIGS[name].with_(**over)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    for seed in range(3):
+        say(f"layer small {name} {over} seed {seed}")
+        b = W.make_block(cfg, seed)
+        out, st = run_layer(lib, cfg, b, w)
+        lg = out["logits_out"].cpu().numpy()
+        lref = O.router_logits(W.to_exact_f64(b.x), W.to_exact_f64(b.w_router),
+                               None if b.b_router is None else b.b_router.numpy())
+        assert np.max(np.abs(lg - lref)) <= 1e-4 * np.max(np.abs(lref))
+        ref = oracle_layer(cfg, b, w, lg)
+        assert check_selection(out, ref, st, cfg, f"{name} seed {seed}")
+        assert st["n_active"] == ref["perm"]["n_active"]
+        assert (out["counts"].cpu().numpy() == ref["perm"]["counts"]).all()
+        err = max_rel_err(out["y"], ref["y"])
+        say(f"  U={st['n_active']} |S|={st['n_eligible']} rel err {err:.2e}")
+        assert err <= TOL[cfg.w], err
+
+
+def test_layer_parity_full_tiny_and_qwen3_30b(lib):
+    for name in ["tiny", "qwen3_30b"]:
+        cfg = W.CONFIGS[name]
+        w = make_weights(cfg, device="cuda", gen_device="cpu" if name == "tiny" else "cuda")
+        for seed in range(2):
+            say(f"layer full {name} seed {seed}")
+            b = W.make_block(cfg, seed)
+            out, st = run_layer(lib, cfg, b, w)
+            ref = oracle_layer(cfg, b, w, out["logits_out"].cpu().numpy())
+            assert check_selection(out, ref, st, cfg, f"{name} seed {seed}")
+            err = max_rel_err(out["y"], ref["y"])
+            say(f"  U={st['n_active']} rel err {err:.2e}")
+            assert err <= TOL[cfg.w]
+
+
+@pytest.mark.parametrize("name,tokens", [("gptoss_120b", [0, 17, 63]),
+                                         ("qwen3_235b", [0, 40]),
+                                         ("dsv31", [0, 129])])
+def test_layer_parity_full_sampled(lib, name, tokens):
+    """Full-size layers: check sampled tokens against the per-token definition
+    y_i = sum_j g_ij E_sel_ij(x_i) (+ shared), plus the whole selection."""
+    cfg = W.CONFIGS[name]
+    say(f"layer full sampled {name}: generating weights")
+    w = make_weights(cfg, device="cuda")
+    b = W.make_block(cfg, 0)
+    out, st = run_layer(lib, cfg, b, w)
+    lg = out["logits_out"].cpu().numpy()
+    ref = oracle_select(cfg, b, logits_in=lg)
+    assert check_selection(out, ref, st, cfg, name)
+    fn = expert_fn_from(cfg, w)
+    y_ref = O.token_outputs(W.to_exact_f64(b.x), ref["topk_idx"], ref["topk_gate"], fn,
+                            shared_fn=shared_fn_from(cfg, w), tokens=tokens)
+    y = out["y"].float().cpu().numpy()[tokens].astype(np.float64)
+    err = float(np.max(np.abs(y - y_ref)) / np.max(np.abs(y_ref)))
+    say(f"  U={st['n_active']} sampled rel err {err:.2e}")
+    assert err <= TOL[cfg.w]
+
+
+def test_separate_entry_points_match_verify_block(lib):
+    """acceptmoe_select -> moe_route_permute -> moe_grouped_swiglu (+ shared)
+    -> moe_combine reproduces verify_block bit for bit."""
+    cfg = W.CONFIGS["dsv31"].with_(E=24, k=4, H=256, I=384, N=32, n_chains=4, chain_len=8)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 2)
+    out, st = run_layer(lib, cfg, b, w)
+    d = upload_block(b)
+    dev = "cuda"
+    sh = shape_of(lib, cfg)
+    N, H, I, E, k = cfg.N, cfg.H, cfg.I, cfg.E, cfg.k
+    e_ = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
+    elig, ti, tg = e_(E, dt=torch.uint8), e_(N, k), e_(N, k, dt=torch.float32)
+    stats = lib.new_stats(dev)
+    ws = torch.empty(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
+    lib.acceptmoe_select(sh, d["x"], d["w_router"], d["b_router"], None, d["parent"],
+                         d["depth"], d["commit"], None, None, elig, ti, tg, stats, ws)
+    counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)
+    lib.moe_route_permute(N, k, E, ti, counts, offsets, sa, ip, act, na)
+    y_perm = e_(N * k, H, dt=torch.float32)
+    gws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, k, I, 2), dtype=torch.uint8,
+                      device=dev)
+    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 2, d["x"], w["w13"], w["w2"], w["s13"], w["s2"],
+                           offsets, sa, act, na, y_perm, gws)
+    # shared expert = one-expert grouped call
+    so = torch.tensor([0, N], dtype=torch.int32, device=dev)
+    ss = torch.arange(N, dtype=torch.int32, device=dev)
+    y_sh = e_(N, H, dt=torch.float32)
+    sws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, 1, I, 2), dtype=torch.uint8,
+                      device=dev)
+    lib.moe_grouped_swiglu(N, 1, 1, H, I, 1, 2, d["x"], w["w13_shared"][None],
+                           w["w2_shared"][None], w["s13_shared"][None], w["s2_shared"][None],
+                           so, ss, torch.zeros(1, dtype=torch.int32, device=dev),
+                           torch.ones(1, dtype=torch.int32, device=dev), y_sh, sws)
+    y = e_(N, H, dt=torch.bfloat16)
+    lib.moe_combine(N, k, H, 1, y_perm, ip, tg, y_sh, y)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, out["topk_idx"]) and torch.equal(tg, out["topk_gate"])
+    assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
+
+
+def test_determinism(lib):
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=64, H=512, I=256, N=64)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 4)
+    o1, s1 = run_layer(lib, cfg, b, w)
+    o2, s2 = run_layer(lib, cfg, b, w)
+    for key in o1:
+        assert torch.equal(o1[key].view(torch.uint8), o2[key].view(torch.uint8)), key
+    assert s1 == s2
+
+
+def test_natural_mode_layer(lib):
+    """Natural routing (all experts eligible) is the standard MoE layer."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=32, H=256, I=192, N=30, flags=1)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 9)
+    out, st = run_layer(lib, cfg, b, w)
+    lg = out["logits_out"].cpu().numpy()
+    ref = oracle_layer(cfg, b, w, lg)
+    assert (out["topk_idx"].cpu().numpy() == O.natural_topk(lg, cfg.k)).all()
+    assert st["n_active"] == st["n_natural_union"]
+    assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]
