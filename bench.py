@@ -195,9 +195,8 @@ def main():
         f"(wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
 
     # ----------------------------------------- per-stage device time (live) --
-    stage_names = {M.STAGE_SELECT: "select", M.STAGE_PERMUTE: "permute",
-                   M.STAGE_GATEUP: "gateup_swiglu", M.STAGE_DOWN: "down",
-                   M.STAGE_COMBINE: "combine"}
+    stage_names = {M.STAGE_SELECT: "select_permute", M.STAGE_GATEUP: "gateup_swiglu",
+                   M.STAGE_DOWN: "down", M.STAGE_COMBINE: "combine"}
     stage_us = {}
     stage_samples = {}
     n_st = max(S, args.stage_steps)

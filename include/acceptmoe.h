@@ -56,6 +56,12 @@ typedef enum {
   ACCEPTMOE_FP8_E4M3FN = 2
 } acceptmoe_dtype;
 
+/* Layout of the expert weights (w13, w2 and the shared expert's). */
+typedef enum {
+  ACCEPTMOE_LAYOUT_ROWMAJOR = 0, /* w13 [E,2,I,H], w2 [E,H,I] as documented below            */
+  ACCEPTMOE_LAYOUT_PACKED = 1    /* reordered once by acceptmoe_pack_experts (BF16 / FP8 only) */
+} acceptmoe_layout;
+
 enum {
   ACCEPTMOE_F_NATURAL = 1u << 0,   /* every expert eligible: natural routing (standard SD) */
   ACCEPTMOE_F_NO_RENORM = 1u << 1, /* gates = raw softmax scores of the chosen experts     */
@@ -84,6 +90,7 @@ typedef struct acceptmoe_shape {
   uint32_t flags;         /* ACCEPTMOE_F_*                                                 */
   int32_t act_dtype;      /* acceptmoe_dtype of x, w_router and y                          */
   int32_t w_dtype;        /* acceptmoe_dtype of the expert weights                         */
+  int32_t w_layout;       /* acceptmoe_layout of the expert weights                        */
 } acceptmoe_shape;
 
 /* Per-block statistics, written by the device. */
@@ -162,6 +169,7 @@ int moe_route_permute(int32_t N, int32_t k, int32_t E, const int32_t* topk_idx, 
  *
  *   x   [N,H] act_dtype
  *   w13 [E,2,I,H] w_dtype (gate rows, then up rows)   w2 [E,H,I] w_dtype
+ *     (or, with w_layout = PACKED, the buffers acceptmoe_pack_experts wrote)
  *   s13 [E,2,I/128,H/128] fp32, s2 [E,H/128,I/128] fp32: FP8 only, else NULL
  *   offsets [E+1], sorted_assign [N*k], active [E], n_active [1]: as written
  *     by moe_route_permute
@@ -172,11 +180,32 @@ int moe_route_permute(int32_t N, int32_t k, int32_t E, const int32_t* topk_idx, 
  * ------------------------------------------------------------------------- */
 size_t moe_grouped_swiglu_workspace_size(int32_t N, int32_t k, int32_t I, int32_t w_dtype);
 int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
-                       int32_t act_dtype, int32_t w_dtype, const void* x, const void* w13,
+                       int32_t act_dtype, int32_t w_dtype, int32_t w_layout, const void* x,
+                       const void* w13,
                        const void* w2, const float* s13, const float* s2,
                        const int32_t* offsets, const int32_t* sorted_assign,
                        const int32_t* active, const int32_t* n_active, float* y_perm,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * acceptmoe_pack_experts -- reorder expert weights into the packed layout.
+ *
+ * Weights are static, so they can be laid out once in the exact order the
+ * gfx950 expert kernels stream them: every load instruction then reads 1 KB
+ * of consecutive bytes and every work-group one contiguous region, which
+ * keeps HBM near its peak ([EcoSpec, Fig. 1]: verification time is the
+ * active experts' weight traffic).  Values are unchanged; the reduction
+ * dimension is zero-padded to a multiple of 128.  FP8 scales keep their
+ * row-major layout.  BF16 and FP8 weights only.
+ *   n_experts  E for the routed experts, 1 for a shared expert
+ *   w13 [n,2,I,H], w2 [n,H,I] row-major (device) -> w13_packed, w2_packed of
+ *   acceptmoe_packed_size(shape, 0, n) and (shape, 1, n) bytes (device);
+ *   either pair may be NULL to pack only the other.
+ * ------------------------------------------------------------------------- */
+size_t acceptmoe_packed_size(const acceptmoe_shape* shape, int32_t which /* 0: w13, 1: w2 */,
+                             int32_t n_experts);
+int acceptmoe_pack_experts(const acceptmoe_shape* shape, int32_t n_experts, const void* w13,
+                           const void* w2, void* w13_packed, void* w2_packed, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_combine -- unpermute and gate-weighted sum.
@@ -241,8 +270,9 @@ int verify_block(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
  * ------------------------------------------------------------------------- */
 enum {
   ACCEPTMOE_STAGE_NONE = 0,
-  ACCEPTMOE_STAGE_SELECT = 1,   /* router, per-node scores, set selection, restricted top-k */
-  ACCEPTMOE_STAGE_PERMUTE = 2,  /* group by expert                                          */
+  ACCEPTMOE_STAGE_SELECT = 1,   /* router, per-node scores, set selection, restricted top-k,
+                                   group by expert                                          */
+  ACCEPTMOE_STAGE_PERMUTE = 2,  /* reserved: grouping runs inside the SELECT stage          */
   ACCEPTMOE_STAGE_GATEUP = 3,   /* routed experts: gate/up projections + SwiGLU             */
   ACCEPTMOE_STAGE_DOWN = 4,     /* routed experts: down projection                          */
   ACCEPTMOE_STAGE_EXPERTS = 5,  /* routed experts: both projections                         */

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libacceptmo
 OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 F_NATURAL, F_NO_RENORM, F_LOGITS_IN = 1, 2, 4
+LAYOUT_ROWMAJOR, LAYOUT_PACKED = 0, 1
 ERR_BAD_TREE, ERR_DEPTH, ERR_NONFINITE, ERR_COMMIT = 1, 2, 4, 8
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3FN,
@@ -38,7 +39,8 @@ class Shape(C.Structure):
     _fields_ = [("N", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32),
                 ("k", C.c_int32), ("n_depth", C.c_int32), ("min_set", C.c_int32),
                 ("fixed_budget", C.c_int32), ("reroute_budget", C.c_int32),
-                ("flags", C.c_uint32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32)]
+                ("flags", C.c_uint32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32),
+                ("w_layout", C.c_int32)]
 
 
 class Inputs(C.Structure):
@@ -70,7 +72,9 @@ def _load():
         "acceptmoe_select": (C.c_int, [vp] + [vp] * 13 + [vp, sz, vp]),
         "moe_route_permute": (C.c_int, [i32, i32, i32] + [vp] * 7 + [vp]),
         "moe_grouped_swiglu_workspace_size": (sz, [i32, i32, i32, i32]),
-        "moe_grouped_swiglu": (C.c_int, [i32] * 7 + [vp] * 10 + [vp, sz, vp]),
+        "moe_grouped_swiglu": (C.c_int, [i32] * 8 + [vp] * 10 + [vp, sz, vp]),
+        "acceptmoe_packed_size": (sz, [vp, i32, i32]),
+        "acceptmoe_pack_experts": (C.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "moe_combine": (C.c_int, [i32] * 4 + [vp] * 5 + [vp]),
         "acceptmoe_workspace_size": (sz, [vp]),
         "verify_block": (C.c_int, [vp, vp, vp, vp, sz, vp]),
@@ -89,6 +93,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
+            "acceptmoe_packed_size", "acceptmoe_pack_experts",
             "acceptmoe_workspace_size", "verify_block", "acceptmoe_set_stage_timer",
             "acceptmoe_strerror",
             "acceptmoe_last_error", "acceptmoe_version")
@@ -151,9 +156,9 @@ def dtype_code(t: torch.dtype) -> int:
 
 
 def make_shape(N, H, I, E, k, n_depth, act_dtype=BF16, w_dtype=BF16, min_set=0,
-               fixed_budget=0, reroute_budget=0, flags=0) -> Shape:
+               fixed_budget=0, reroute_budget=0, flags=0, w_layout=LAYOUT_ROWMAJOR) -> Shape:
     return Shape(N, H, I, E, k, n_depth, min_set, fixed_budget, reroute_budget, flags,
-                 act_dtype, w_dtype)
+                 act_dtype, w_dtype, w_layout)
 
 
 def decode_stats(t: torch.Tensor) -> dict:
@@ -222,15 +227,18 @@ def moe_grouped_swiglu_workspace_size(N, k, I, w_dtype) -> int:
 
 
 def moe_grouped_swiglu(N, k, E, H, I, act_dtype, w_dtype, x, w13, w2, s13, s2, offsets,
-                       sorted_assign, active, n_active, y_perm, ws, stream=None):
+                       sorted_assign, active, n_active, y_perm, ws, stream=None,
+                       w_layout=LAYOUT_ROWMAJOR):
     adt = torch.float32 if act_dtype == F32 else torch.bfloat16
     wdt = {F32: torch.float32, BF16: torch.bfloat16,
            FP8_E4M3FN: (torch.uint8, torch.float8_e4m3fn)}[w_dtype]
     i32 = torch.int32
     fp8 = w_dtype == FP8_E4M3FN
+    packed = w_layout == LAYOUT_PACKED
     _check(_lib.moe_grouped_swiglu(
-        N, k, E, H, I, act_dtype, w_dtype, _ptr(x, "x", adt, (N, H)),
-        _ptr(w13, "w13", wdt, (E, 2, I, H)), _ptr(w2, "w2", wdt, (E, H, I)),
+        N, k, E, H, I, act_dtype, w_dtype, w_layout, _ptr(x, "x", adt, (N, H)),
+        _ptr(w13, "w13", torch.uint8 if packed else wdt, None if packed else (E, 2, I, H)),
+        _ptr(w2, "w2", torch.uint8 if packed else wdt, None if packed else (E, H, I)),
         _ptr(s13, "s13", torch.float32, (E, 2, I // 128, H // 128) if fp8 else None),
         _ptr(s2, "s2", torch.float32, (E, H // 128, I // 128) if fp8 else None),
         _ptr(offsets, "offsets", i32, (E + 1,)),
@@ -250,6 +258,32 @@ def moe_combine(N, k, H, act_dtype, y_perm, inv_pos, topk_gate, y_shared, y, str
         _stream(stream)), "moe_combine")
 
 
+# ----------------------------------------------------------------- packing --
+def acceptmoe_packed_size(shape: Shape, which: int, n_experts: int) -> int:
+    return int(_lib.acceptmoe_packed_size(C.byref(shape), which, n_experts))
+
+
+def acceptmoe_pack_experts(shape: Shape, n_experts: int, w13, w2, w13_packed, w2_packed,
+                           stream=None):
+    wdt = {BF16: torch.bfloat16, FP8_E4M3FN: (torch.uint8, torch.float8_e4m3fn)}.get(shape.w_dtype)
+    H, I = shape.H, shape.I
+    _check(_lib.acceptmoe_pack_experts(
+        C.byref(shape), n_experts, _ptr(w13, "w13", wdt, (n_experts, 2, I, H)),
+        _ptr(w2, "w2", wdt, (n_experts, H, I)),
+        _ptr(w13_packed, "w13_packed", torch.uint8, (acceptmoe_packed_size(shape, 0, n_experts),)),
+        _ptr(w2_packed, "w2_packed", torch.uint8, (acceptmoe_packed_size(shape, 1, n_experts),)),
+        _stream(stream)), "acceptmoe_pack_experts")
+
+
+def pack_experts(shape: Shape, w13, w2, n_experts: int, stream=None):
+    """Allocate (torch) and fill the packed copies of w13 / w2."""
+    dev = w13.device
+    p13 = torch.empty(acceptmoe_packed_size(shape, 0, n_experts), dtype=torch.uint8, device=dev)
+    p2 = torch.empty(acceptmoe_packed_size(shape, 1, n_experts), dtype=torch.uint8, device=dev)
+    acceptmoe_pack_experts(shape, n_experts, w13.contiguous(), w2.contiguous(), p13, p2, stream)
+    return p13, p2
+
+
 # ------------------------------------------------------------ whole block --
 def acceptmoe_workspace_size(shape: Shape) -> int:
     return int(_lib.acceptmoe_workspace_size(C.byref(shape)))
@@ -259,7 +293,8 @@ def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
     """inputs/outputs: dicts keyed like acceptmoe_inputs / acceptmoe_outputs."""
     N, H, I, E, k = shape.N, shape.H, shape.I, shape.E, shape.k
     adt = _act_dt(shape)
-    wdt = _w_dt(shape)
+    packed = shape.w_layout == LAYOUT_PACKED
+    wdt = torch.uint8 if packed else _w_dt(shape)
     fp8 = shape.w_dtype == FP8_E4M3FN
     g = inputs.get
     inp = Inputs(
@@ -270,11 +305,12 @@ def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
         _ptr(g("depth"), "depth", torch.int32, (N,)),
         _ptr(g("commit"), "commit", torch.float32, (shape.n_depth,)),
         _ptr(g("resident"), "resident", torch.uint8, (E,)),
-        _ptr(g("w13"), "w13", wdt, (E, 2, I, H)), _ptr(g("w2"), "w2", wdt, (E, H, I)),
+        _ptr(g("w13"), "w13", wdt, None if packed else (E, 2, I, H)),
+        _ptr(g("w2"), "w2", wdt, None if packed else (E, H, I)),
         _ptr(g("s13"), "s13", torch.float32, (E, 2, I // 128, H // 128) if fp8 else None),
         _ptr(g("s2"), "s2", torch.float32, (E, H // 128, I // 128) if fp8 else None),
-        _ptr(g("w13_shared"), "w13_shared", wdt, (2, I, H)),
-        _ptr(g("w2_shared"), "w2_shared", wdt, (H, I)),
+        _ptr(g("w13_shared"), "w13_shared", wdt, None if packed else (2, I, H)),
+        _ptr(g("w2_shared"), "w2_shared", wdt, None if packed else (H, I)),
         _ptr(g("s13_shared"), "s13_shared", torch.float32, (2, I // 128, H // 128) if fp8 else None),
         _ptr(g("s2_shared"), "s2_shared", torch.float32, (H // 128, I // 128) if fp8 else None))
     o = outputs.get

@@ -36,6 +36,15 @@ struct SelectArgs {
   int32_t* nat;      // [N][k]
   double* contrib;   // [N][E]
   int32_t* node_err; // [N]
+  int32_t* counters; // [2]: node-kernel and restricted-kernel arrival counters
+  // when non-null, the restricted kernel's last work-group also groups the
+  // assignments by expert (moe_route_permute's outputs)
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_assign;
+  int32_t* inv_pos;
+  int32_t* active;
+  int32_t* n_active;
 };
 
 // router partial products, per-node softmax / natural top-k / demand terms,
@@ -66,9 +75,16 @@ struct GroupedArgs {
   float* y_perm;
   void* h_perm;  // [N*k][I] bf16 (fp32 when w_kind == 0)
   int num_cu;
+  int packed;    // w13 / w2 are in the packed layout (pack_experts)
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);
+
+// Packed expert layout (bf16 / fp8 weights): see grouped.hip.  which: 0 for
+// w13 ([E,2,I,H] -> packed), 1 for w2 ([E,H,I] -> packed).
+size_t packed_bytes(int which, int w_kind, int E, int H, int I);
+hipError_t launch_pack(int which, int w_kind, int E, int H, int I, const void* src, void* dst,
+                       hipStream_t stream);
 
 hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm,
                           const int32_t* inv_pos, const float* topk_gate, const float* y_shared,

@@ -89,6 +89,10 @@ int check_shape(const acceptmoe_shape* s, bool need_i) {
     return fail(ACCEPTMOE_ENOTSUP, "unsupported dtype pair (act %d, weights %d)", s->act_dtype,
                 s->w_dtype);
   if (s->flags & ~7u) return fail(ACCEPTMOE_ENOTSUP, "unknown flag bits %#x", s->flags);
+  if (s->w_layout != ACCEPTMOE_LAYOUT_ROWMAJOR && s->w_layout != ACCEPTMOE_LAYOUT_PACKED)
+    return fail(ACCEPTMOE_ENOTSUP, "unknown weight layout %d", s->w_layout);
+  if (s->w_layout == ACCEPTMOE_LAYOUT_PACKED && s->w_dtype == ACCEPTMOE_F32)
+    return fail(ACCEPTMOE_ENOTSUP, "the packed layout needs BF16 or FP8 weights");
   int rc = check_sizes(s->N, s->k, s->E, s->H, s->I, s->w_dtype, true, need_i);
   if (rc) return rc;
   if (s->n_depth < 1) return fail(ACCEPTMOE_EINVAL, "n_depth=%d < 1", s->n_depth);
@@ -109,6 +113,7 @@ struct SelectWs {
   int32_t* nat;
   double* contrib;
   int32_t* node_err;
+  int32_t* counters;
   int ksplit, kslice;
 };
 
@@ -123,6 +128,7 @@ SelectWs carve_select(Carver& c, const acceptmoe_shape* s) {
   w.nat = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
   w.contrib = c.take<double>(NE);
   w.node_err = c.take<int32_t>(s->N);
+  w.counters = c.take<int32_t>(2);
   return w;
 }
 
@@ -208,6 +214,7 @@ amoe::SelectArgs select_args(const acceptmoe_shape* s, const SelectWs& w) {
   a.nat = w.nat;
   a.contrib = w.contrib;
   a.node_err = w.node_err;
+  a.counters = w.counters;
   return a;
 }
 
@@ -306,14 +313,18 @@ size_t moe_grouped_swiglu_workspace_size(int32_t N, int32_t k, int32_t I, int32_
 }
 
 int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
-                       int32_t act_dtype, int32_t w_dtype, const void* x, const void* w13,
-                       const void* w2, const float* s13, const float* s2,
+                       int32_t act_dtype, int32_t w_dtype, int32_t w_layout, const void* x,
+                       const void* w13, const void* w2, const float* s13, const float* s2,
                        const int32_t* offsets, const int32_t* sorted_assign,
                        const int32_t* active, const int32_t* n_active, float* y_perm,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_pair_ok(act_dtype, w_dtype))
     return fail(ACCEPTMOE_ENOTSUP, "unsupported dtype pair (act %d, weights %d)", act_dtype,
                 w_dtype);
+  if (w_layout != ACCEPTMOE_LAYOUT_ROWMAJOR && w_layout != ACCEPTMOE_LAYOUT_PACKED)
+    return fail(ACCEPTMOE_ENOTSUP, "unknown weight layout %d", w_layout);
+  if (w_layout == ACCEPTMOE_LAYOUT_PACKED && w_dtype == ACCEPTMOE_F32)
+    return fail(ACCEPTMOE_ENOTSUP, "the packed layout needs BF16 or FP8 weights");
   // the shared expert is a call with E = 1, k = 1
   if (N < 1 || N > 4096) return fail(ACCEPTMOE_EINVAL, "N=%d outside [1, 4096]", N);
   if (k < 1 || k > 16 || E < 1 || E > 256)
@@ -347,6 +358,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.y_perm = y_perm;
   a.h_perm = ws;
   a.num_cu = num_cu();
+  a.packed = w_layout == ACCEPTMOE_LAYOUT_PACKED;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -362,6 +374,38 @@ int moe_combine(int32_t N, int32_t k, int32_t H, int32_t act_dtype, const float*
   return hip_status(amoe::launch_combine(N, k, H, act_dtype == ACCEPTMOE_BF16, y_perm, inv_pos,
                                          topk_gate, y_shared, y, stream),
                     "moe_combine");
+}
+
+size_t acceptmoe_packed_size(const acceptmoe_shape* s, int32_t which, int32_t n_experts) {
+  if (check_shape(s, true)) return 0;
+  if (s->w_dtype == ACCEPTMOE_F32 || (which != 0 && which != 1) || n_experts < 1 ||
+      n_experts > 256)
+    return 0;
+  return amoe::packed_bytes(which, w_kind(s->w_dtype), n_experts, s->H, s->I);
+}
+
+int acceptmoe_pack_experts(const acceptmoe_shape* s, int32_t n_experts, const void* w13,
+                           const void* w2, void* w13_packed, void* w2_packed,
+                           hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc) return rc;
+  if (s->w_dtype == ACCEPTMOE_F32)
+    return fail(ACCEPTMOE_ENOTSUP, "the packed layout needs BF16 or FP8 weights");
+  if (n_experts < 1 || n_experts > 256)
+    return fail(ACCEPTMOE_EINVAL, "n_experts=%d outside [1, 256]", n_experts);
+  if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr) ||
+      (!w13 && !w2))
+    return fail(ACCEPTMOE_EINVAL, "give a source and a destination for w13 and/or w2");
+  const int wk = w_kind(s->w_dtype);
+  if (w13) {
+    rc = hip_status(amoe::launch_pack(0, wk, n_experts, s->H, s->I, w13, w13_packed, stream),
+                    "acceptmoe_pack_experts/w13");
+    if (rc) return rc;
+  }
+  if (w2)
+    rc = hip_status(amoe::launch_pack(1, wk, n_experts, s->H, s->I, w2, w2_packed, stream),
+                    "acceptmoe_pack_experts/w2");
+  return rc;
 }
 
 size_t acceptmoe_workspace_size(const acceptmoe_shape* s) {
@@ -413,17 +457,17 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.topk_idx = topk_idx;
   a.topk_gate = topk_gate;
   a.stats = stats;
+  // the restricted top-k kernel's last work-group also groups by expert
+  a.counts = counts;
+  a.offsets = w.offsets;
+  a.sorted_assign = w.sorted_assign;
+  a.inv_pos = w.inv_pos;
+  a.active = active;
+  a.n_active = w.n_active;
   timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
   rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
   if (rc) return rc;
   timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
-  timer_mark(ACCEPTMOE_STAGE_PERMUTE, true, stream);
-  rc = hip_status(amoe::launch_permute(s->N, s->k, s->E, topk_idx, counts, w.offsets,
-                                       w.sorted_assign, w.inv_pos, active, w.n_active,
-                                       in->resident, stats, stream),
-                  "verify_block/permute");
-  if (rc) return rc;
-  timer_mark(ACCEPTMOE_STAGE_PERMUTE, false, stream);
   amoe::GroupedArgs g;
   g.N = s->N;
   g.k = s->k;
@@ -444,6 +488,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.y_perm = w.y_perm;
   g.h_perm = w.h_perm;
   g.num_cu = num_cu();
+  g.packed = s->w_layout == ACCEPTMOE_LAYOUT_PACKED;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
   rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");

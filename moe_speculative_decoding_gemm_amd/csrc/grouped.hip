@@ -30,6 +30,8 @@
 // are widened to bf16 exactly (scale 1) and the per-128x128-block scale is
 // applied to each 128-long partial sum.
 
+#include <type_traits>
+
 #include "amoe_common.h"
 #include "amoe_launch.h"
 
@@ -38,6 +40,8 @@ namespace amoe {
 namespace {
 
 constexpr int kMT = 4;  // M tiles (16 rows each) per pass over the weights
+constexpr int kPackChunk = 128;  // reduction elements per packed chunk
+constexpr int kFragElems = 512;  // elements of one packed MFMA B fragment
 
 // ---- operand fragments --------------------------------------------------
 // 8 consecutive reduction elements of one row, as the MFMA wants them
@@ -356,6 +360,343 @@ __global__ __launch_bounds__(256) void down_kernel(GroupedArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------
+// Work-group items with the activation rows staged in LDS (bf16 / fp8
+// weights with bf16 activations).
+//
+// One work-group (4 waves) owns 64*NT weight rows of one active expert (wave
+// w: N tiles w*NT .. w*NT+NT-1 of 16 rows) over the full reduction length K,
+// for up to 64 routed rows at a time.  The routed rows' activations are
+// staged into LDS in chunks of KC reduction elements (double buffered, one
+// barrier per chunk) and shared by the 4 waves; each wave keeps its weight
+// fragments for the next chunk in flight in registers (ping-pong).  Loads are
+// issued in the order they are consumed -- next activation chunk, then next
+// weight chunk, then compute the current chunk -- so the in-order vmcnt
+// waits never stall on a newer load.
+template <int WK>
+struct BRaw;
+template <>
+struct BRaw<1> {
+  using T = u32x4_t;  // 8 bf16
+};
+template <>
+struct BRaw<2> {
+  using T = u32x2_t;  // 8 fp8
+};
+
+__device__ __forceinline__ bf16x8_t to_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t to_bf16x8(const u32x2_t& u) {
+  const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[0], 1.0f, false);
+  const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[0], 1.0f, true);
+  const bf16x2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[1], 1.0f, false);
+  const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u[1], 1.0f, true);
+  bf16x8_t f;
+  f[0] = q0[0];
+  f[1] = q0[1];
+  f[2] = q1[0];
+  f[3] = q1[1];
+  f[4] = q2[0];
+  f[5] = q2[1];
+  f[6] = q3[0];
+  f[7] = q3[1];
+  return f;
+}
+
+template <int WK, bool GATEUP, int NT, int KC, bool PACKED>
+__global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
+  static_assert(!PACKED || KC == kPackChunk, "packed weights come in 128-long chunks");
+  constexpr int MT = 4;
+  constexpr int ROWS = 16 * MT;
+  constexpr int STEPS = KC / 32;
+  constexpr int LDK = KC + 8;         // LDS row stride in bf16 elements (16 B pad)
+  constexpr int TPR = KC / 8;         // threads per staged row, 16 B each
+  constexpr int RPP = 256 / TPR;      // staged rows per pass
+  constexpr int PASSES = ROWS / RPP;
+  using WTp = typename WeightT<WK>::T;
+  using BR = typename BRaw<WK>::T;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * LDK];
+
+  const int H = a.H, I = a.I, k = a.k;
+  const int K = GATEUP ? H : I;
+  const int tiles = (GATEUP ? 2 * I : H) / (64 * NT);
+  const int n_items = *a.n_active * tiles;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 15, g = lane >> 4;
+  const int nchunks = (K + KC - 1) / KC;
+  // packed weights are zero-padded to whole chunks: every step is computed
+  const int nsteps = PACKED ? nchunks * STEPS : (K >> 5);
+  const WTp* w13 = static_cast<const WTp*>(a.w13);
+  const WTp* w2 = static_cast<const WTp*>(a.w2);
+  const uint16_t* src_base = static_cast<const uint16_t*>(GATEUP ? a.x : a.h_perm);
+  const int src_ld = GATEUP ? H : I;
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int u = item / tiles;
+    const int tile = item - u * tiles;
+    const int e = a.active[u];
+    const int off = a.offsets[e];
+    const int te = a.offsets[e + 1] - off;
+
+    const WTp* wrow[NT];
+    int orow[NT];   // gate/up: intermediate index i; down: hidden index h
+    int srow[NT];   // row of the weight matrix selected by the scale grid
+    int half = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int q = (tile * 4 + wave) * NT + nt;  // 16-row tile index within the expert
+      if (GATEUP) {
+        half = r >> 3;
+        const int irow = q * 8 + (r & 7);
+        orow[nt] = irow;
+        srow[nt] = (e * 2 + half) * (I >> 7) + (irow >> 7);
+        wrow[nt] = w13 + (static_cast<size_t>(e * 2 + half) * I + irow) * H + 8 * g;
+      } else {
+        const int hrow = q * 16 + r;
+        orow[nt] = hrow;
+        srow[nt] = e * (H >> 7) + (hrow >> 7);
+        wrow[nt] = w2 + (static_cast<size_t>(e) * H + hrow) * I + 8 * g;
+      }
+    }
+    const float* scales = GATEUP ? a.s13 : a.s2;
+    const int nkb = K >> 7;
+    // packed: this wave's fragments of the item, chunk-major (see pack_kernel)
+    const WTp* pbase = static_cast<const WTp*>(GATEUP ? a.w13 : a.w2) +
+                       (static_cast<size_t>(e) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
+                       static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
+
+    for (int mg = 0; mg < te; mg += ROWS) {
+      const int mt_n = min(MT, (te - mg + 15) >> 4);
+      // Staging sources, PASSES rows per thread.  Rows past the routed ones
+      // read row 0 of the group instead (their results are never stored), so
+      // every load below is unconditional: guarded loads would make the
+      // compiler's wait counting fall back to waiting for all of them.
+      const uint16_t* src[PASSES];
+      const int kk = (t % TPR) * 8;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int rr = p * RPP + t / TPR;
+        const int m = mg + rr < te ? mg + rr : mg;
+        const int srcrow = GATEUP ? a.sorted_assign[off + m] / k : off + m;
+        src[p] = src_base + static_cast<size_t>(srcrow) * src_ld;
+      }
+      f32x4_t acc[NT][MT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      // Pipeline, two chunks deep for both operands: activation chunk c waits
+      // in a VGPR ring of 2 until the end of chunk c-1, when it is written to
+      // LDS buffer c%2; weight chunk c waits in a VGPR ring of 2.  Issue order
+      // per chunk c: activations of c+2, compute c, weights of c+2, then store
+      // activations of c+1.  That store waits for activations c+1 and the
+      // loads older than them (vmcnt retires in issue order); weights c+1 were
+      // issued after activations c+1, so no wait ever stalls on weights that
+      // are not needed yet.  All loads of the steady state are unconditional;
+      // columns and steps past K are clamped to valid addresses whose data is
+      // never used.
+      u32x4_t sv[2][PASSES];
+      auto stage_load = [&](u32x4_t (&v)[PASSES], int c) {
+        const int k0 = min(c * KC + kk, K - 8);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) v[p] = *reinterpret_cast<const u32x4_t*>(src[p] + k0);
+      };
+      auto stage_store = [&](const u32x4_t (&v)[PASSES], int buf) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const int rr = p * RPP + t / TPR;
+          *reinterpret_cast<u32x4_t*>(&sA[buf][rr * LDK + kk]) = v[p];
+        }
+      };
+      auto load_b = [&](BR (&b)[STEPS][NT], int c) {
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j) {
+          if (PACKED) {
+            const WTp* f = pbase + static_cast<size_t>((min(c, nchunks - 1) * 4 + j) * 4 * NT) * kFragElems;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(f + nt * kFragElems));
+          } else {
+            const int s = min(c * STEPS + j, nsteps - 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(wrow[nt] + s * 32));
+          }
+        }
+      };
+      auto compute = [&](const BR (&b)[STEPS][NT], int c, int buf) {
+        const int kb = (c * KC) >> 7;  // FP8 scale block (KC == 128 for FP8)
+        f32x4_t tmp[NT][MT];
+        if (WK == 2) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) tmp[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j) {
+          if (c * STEPS + j >= nsteps) break;
+          bf16x8_t bf[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) bf[nt] = to_bf16x8(b[j][nt]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            if (mt >= mt_n) break;
+            const bf16x8_t af = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(&sA[buf][(mt * 16 + r) * LDK + 32 * j + 8 * g]));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              if (WK == 2)
+                tmp[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], tmp[nt][mt], 0, 0, 0);
+              else
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], acc[nt][mt], 0, 0, 0);
+            }
+          }
+        }
+        if (WK == 2) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float sc = scales[static_cast<size_t>(srow[nt]) * nkb + kb];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += sc * tmp[nt][mt];
+          }
+        }
+      };
+
+      BR bq[2][STEPS][NT];
+      // prologue: A0 B0 A1 B1
+      stage_load(sv[0], 0);
+      load_b(bq[0], 0);
+      stage_load(sv[1], min(1, nchunks - 1));
+      load_b(bq[1], min(1, nchunks - 1));
+      stage_store(sv[0], 0);
+      __syncthreads();
+      auto body_main = [&](auto ic, int c) {
+        constexpr int i = decltype(ic)::value;
+        stage_load(sv[i], c + 2);
+        compute(bq[i], c, i);
+        load_b(bq[i], c + 2);
+        stage_store(sv[i ^ 1], i ^ 1);
+        __syncthreads();
+      };
+      auto body_tail = [&](auto ic, int c) {
+        constexpr int i = decltype(ic)::value;
+        if (c + 2 < nchunks) stage_load(sv[i], c + 2);
+        compute(bq[i], c, i);
+        if (c + 2 < nchunks) load_b(bq[i], c + 2);
+        if (c + 1 < nchunks) stage_store(sv[i ^ 1], i ^ 1);
+        __syncthreads();
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      int c = 0;
+      for (; c + 4 <= nchunks; c += 2) {  // chunks c, c+1 both prefetch (c+3 < nchunks)
+        body_main(I0{}, c);
+        body_main(I1{}, c + 1);
+      }
+      // 0..3 chunks remain; c is even
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (c + q >= nchunks) break;
+        if ((q & 1) == 0)
+          body_tail(I0{}, c + q);
+        else
+          body_tail(I1{}, c + q);
+      }
+
+      // epilogue: lane (r, g) holds D[m = 4g + j][n = r] of each tile
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt >= mt_n) break;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int m = mg + 16 * mt + 4 * g + j;
+            const float v = acc[nt][mt][j];
+            if (GATEUP) {
+              const float up = __shfl_xor(v, 8, kWave);
+              if (half == 0 && m < te)
+                static_cast<uint16_t*>(a.h_perm)[static_cast<size_t>(off + m) * I + orow[nt]] =
+                    f32_to_bf16(silu(v) * up);
+            } else if (m < te) {
+              a.y_perm[static_cast<size_t>(off + m) * H + orow[nt]] = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Packed expert layout.  Weights are static, so they are reordered once
+// (at load time) into exactly the order the expert kernels read them: each
+// wave load instruction then reads 1 KB of consecutive bytes and each
+// work-group streams one contiguous region, which is what lets HBM run near
+// its peak (16-row x 64-byte fragment reads of row-major weights scatter
+// every instruction over 16 DRAM locations).
+//
+// Unit: a fragment = the B operand of one 16x16x32 MFMA for one 16-row tile
+// and 32 reduction elements, stored lane-major (lane l = r + 16g holds the 8
+// elements row(r), k = 32*step + 8g .. +7): 512 elements.  Tile q of an
+// expert is rows 16q..16q+15 of w2, or for w13 the 8 gate rows 8q..8q+7
+// followed by the 8 up rows 8q..8q+7.  A group = the 4*NT tiles of one
+// work-group item (wave w: tiles w*NT .. w*NT+NT-1).  Order:
+//   [expert][group][chunk of 128][step (4)][wave (4)][tile nt (NT)][lane][8]
+// The reduction dimension is zero-padded to whole chunks.
+constexpr int kPackNT_bf16 = 1;
+constexpr int kPackNT_fp8 = 2;
+
+template <int WK, bool GATEUP>
+__global__ __launch_bounds__(256) void pack_kernel(const typename WeightT<WK>::T* __restrict__ src,
+                                                   typename WeightT<WK>::T* __restrict__ dst,
+                                                   int E, int H, int I) {
+  using WTp = typename WeightT<WK>::T;
+  constexpr int NT = WK == 2 ? kPackNT_fp8 : kPackNT_bf16;
+  const int K = GATEUP ? H : I;
+  const int nC = (K + kPackChunk - 1) / kPackChunk;
+  const int nG = (GATEUP ? 2 * I : H) / (64 * NT);
+  const size_t units = static_cast<size_t>(E) * nG * nC * 16 * NT * 64;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= units) return;
+  size_t rest = idx;
+  const int lane = static_cast<int>(rest % 64);
+  rest /= 64;
+  const int nt = static_cast<int>(rest % NT);
+  rest /= NT;
+  const int w = static_cast<int>(rest % 4);
+  rest /= 4;
+  const int j = static_cast<int>(rest % 4);
+  rest /= 4;
+  const int c = static_cast<int>(rest % nC);
+  rest /= nC;
+  const int G = static_cast<int>(rest % nG);
+  const int e = static_cast<int>(rest / nG);
+  const int q = (G * 4 + w) * NT + nt;
+  const int r = lane & 15, g = lane >> 4;
+  const int k = c * kPackChunk + 32 * j + 8 * g;
+  const WTp* row;
+  if (GATEUP) {
+    const int half = r >> 3;
+    row = src + (static_cast<size_t>(e * 2 + half) * I + q * 8 + (r & 7)) * H;
+  } else {
+    row = src + (static_cast<size_t>(e) * H + q * 16 + r) * I;
+  }
+  WTp* out = dst + idx * 8;
+  if (WK == 2) {
+    u32x2_t v = {0u, 0u};
+    if (k < K) v = *reinterpret_cast<const u32x2_t*>(row + k);
+    *reinterpret_cast<u32x2_t*>(out) = v;
+  } else {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (k < K) v = *reinterpret_cast<const u32x4_t*>(row + k);
+    *reinterpret_cast<u32x4_t*>(out) = v;
+  }
+}
+
 }  // namespace
 
 template <int WK>
@@ -365,17 +706,80 @@ void launch_wk(const GroupedArgs& a, hipStream_t stream, int which) {
   if (which != 1) down_kernel<WK><<<blocks, 256, 0, stream>>>(a);
 }
 
+// resident work-groups per CU of one kernel (queried once per process)
+template <typename Kern>
+int resident_per_cu(Kern kern, int fallback) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n <= 0)
+    n = fallback;
+  return n;
+}
+
+template <int WK, int NT, int KC, bool PACKED>
+void launch_lds(const GroupedArgs& a, hipStream_t stream, int which) {
+  static const int occ_g = resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED>, 2);
+  static const int occ_d = resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED>, 2);
+  const int max_active = a.E < a.N * a.k ? a.E : a.N * a.k;
+  if (which != 2) {
+    const int items = max_active * (2 * a.I / (64 * NT));
+    const int grid = items < occ_g * a.num_cu ? items : occ_g * a.num_cu;
+    expert_lds_kernel<WK, true, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
+  }
+  if (which != 1) {
+    const int items = max_active * (a.H / (64 * NT));
+    const int grid = items < occ_d * a.num_cu ? items : occ_d * a.num_cu;
+    expert_lds_kernel<WK, false, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
+  }
+}
+
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which) {
   switch (a.w_kind) {
     case 0:
       launch_wk<0>(a, stream, which);
       break;
     case 1:
-      launch_wk<1>(a, stream, which);
+      if (a.packed)
+        launch_lds<1, kPackNT_bf16, kPackChunk, true>(a, stream, which);
+      else
+        launch_lds<1, 1, 128, false>(a, stream, which);
       break;
     default:
-      launch_wk<2>(a, stream, which);
+      if (a.packed)
+        launch_lds<2, kPackNT_fp8, kPackChunk, true>(a, stream, which);
+      else
+        launch_lds<2, 2, 128, false>(a, stream, which);
       break;
+  }
+  return hipGetLastError();
+}
+
+size_t packed_bytes(int which, int w_kind, int E, int H, int I) {
+  const int NT = w_kind == 2 ? kPackNT_fp8 : kPackNT_bf16;
+  const int esize = w_kind == 2 ? 1 : 2;
+  const int K = which == 0 ? H : I;
+  const size_t nC = (K + kPackChunk - 1) / kPackChunk;
+  const size_t nG = (which == 0 ? 2 * static_cast<size_t>(I) : H) / (64 * NT);
+  return static_cast<size_t>(E) * nG * nC * 16 * NT * kFragElems * esize;
+}
+
+hipError_t launch_pack(int which, int w_kind, int E, int H, int I, const void* src, void* dst,
+                       hipStream_t stream) {
+  const size_t units = packed_bytes(which, w_kind, E, H, I) / ((w_kind == 2 ? 1 : 2) * 8);
+  const unsigned blocks = static_cast<unsigned>((units + 255) / 256);
+  if (w_kind == 2) {
+    if (which == 0)
+      pack_kernel<2, true><<<blocks, 256, 0, stream>>>(static_cast<const uint8_t*>(src),
+                                                       static_cast<uint8_t*>(dst), E, H, I);
+    else
+      pack_kernel<2, false><<<blocks, 256, 0, stream>>>(static_cast<const uint8_t*>(src),
+                                                        static_cast<uint8_t*>(dst), E, H, I);
+  } else {
+    if (which == 0)
+      pack_kernel<1, true><<<blocks, 256, 0, stream>>>(static_cast<const uint16_t*>(src),
+                                                       static_cast<uint16_t*>(dst), E, H, I);
+    else
+      pack_kernel<1, false><<<blocks, 256, 0, stream>>>(static_cast<const uint16_t*>(src),
+                                                        static_cast<uint16_t*>(dst), E, H, I);
   }
   return hipGetLastError();
 }

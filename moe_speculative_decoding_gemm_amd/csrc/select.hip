@@ -7,21 +7,28 @@
 // root anchor, self-sizing by effective rank and residency-aware pruning;
 // [AcceptMoE abstract] for restricting top-k to the eligible set.
 //
-// Four kernels, all wave64:
+// Three kernels, all wave64:
 //   router_partial  grid (E/64, N/64, ksplit): 64x64 logit tile over one K slice
-//                   per work-group, fp32 FMA from LDS (no MFMA: the router is a
-//                   few MFLOP at batch one and a tile read at most once per CU).
-//   node            one wave per node: sum of K-slice partials + bias, fp64
-//                   softmax statistics, natural top-k by 64-bit (logit, ~index)
-//                   keys, dense demand terms c[depth] * p for the node's top-k.
-//   select_set      one 1024-thread work-group: demand per expert (fixed
+//                   per work-group, fp32 FMA from LDS (vector ALU: the router is
+//                   a few MFLOP at batch one; matrix cores are kept for the
+//                   expert contractions).
+//   node            one wave per node (16 per work-group): sum of the K-slice
+//                   partials + bias, fp64 softmax statistics, natural top-k by
+//                   64-bit (logit, ~index) keys, dense demand terms
+//                   c[depth] * p for the node's top-k.  The last work-group to
+//                   finish then selects the set: demand per expert (fixed
 //                   summation order), entropy, set size, anchor + fill by rank
 //                   counting, pruning by rank counting, statistics.
-//   restricted      one wave per node: top-k over the eligible experts, gates.
-// Every reduction has a fixed order, so two runs give identical bits.
+//   restricted      one wave per node: top-k over the eligible experts and the
+//                   gates; the last work-group to finish groups the
+//                   assignments by expert (verify_block only).
+// Arrival counters are reset by the kernel before, in stream order, so no
+// memset is needed.  Every reduction has a fixed order: two runs give
+// identical bits.
 
 #include "amoe_common.h"
 #include "amoe_launch.h"
+#include "amoe_permute.h"
 
 namespace amoe {
 
@@ -57,10 +64,14 @@ template <typename AT>
 __global__ __launch_bounds__(256) void router_partial_kernel(const AT* __restrict__ x,
                                                              const AT* __restrict__ w, int N,
                                                              int E, int H, int kslice,
-                                                             float* __restrict__ part) {
+                                                             float* __restrict__ part,
+                                                             int32_t* __restrict__ counters,
+                                                             int compute) {
   __shared__ float xs[kRKC][kRT + 4];
   __shared__ float wsm[kRKC][kRT + 4];
   const int t = threadIdx.x;
+  if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) counters[0] = 0;
+  if (!compute) return;
   const int e0 = blockIdx.x * kRT, n0 = blockIdx.y * kRT, ks = blockIdx.z;
   const int kbeg = ks * kslice;
   const int kend = min(H, kbeg + kslice);
@@ -116,109 +127,117 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const AT* __restric
   }
 }
 
-// one wave per node
-__global__ __launch_bounds__(256) void node_kernel(SelectArgs a) {
+// set selection by one 1024-thread work-group (the last node work-group)
+__device__ void select_set(const SelectArgs& a);
+
+// one wave per node, 16 nodes per work-group
+__global__ __launch_bounds__(1024) void node_kernel(SelectArgs a) {
   const int lane = lane_id();
-  const int i = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
-  if (i >= a.N) return;
-  const int E = a.E, k = a.k;
-  const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
-
-  float l[4];
-  bool valid[4];
-  bool nonfinite = false;
+  const int i = blockIdx.x * 16 + static_cast<int>(threadIdx.x >> 6);
+  if (threadIdx.x == 0 && blockIdx.x == 0) a.counters[1] = 0;
+  if (i < a.N) {
+    const int E = a.E, k = a.k;
+    const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
+    float l[4];
+    bool valid[4];
+    bool nonfinite = false;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + kWave * q;
-    valid[q] = e < E;
-    float v = 0.f;
-    if (valid[q]) {
-      if (logits_in) {
-        v = a.logits_in[static_cast<size_t>(i) * E + e];
-      } else {
-        float s = 0.f;
-        for (int ks = 0; ks < a.ksplit; ++ks)
-          s += a.part[(static_cast<size_t>(ks) * a.N + i) * E + e];
-        v = s + (a.b_router ? a.b_router[e] : 0.f);
-      }
-      a.logits[static_cast<size_t>(i) * E + e] = v;
-      if (a.logits_out) a.logits_out[static_cast<size_t>(i) * E + e] = v;
-      if (!isfinite(v)) nonfinite = true;
-    }
-    l[q] = v;
-  }
-  float m = -INFINITY;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + kWave * q;
+      valid[q] = e < E;
+      float v = 0.f;
+      if (valid[q]) {
+        if (logits_in) {
+          v = a.logits_in[static_cast<size_t>(i) * E + e];
+        } else {
+          // partial sums in K-slice order; loads issued eight at a time
+          const float* p = a.part + static_cast<size_t>(i) * E + e;
+          const size_t stride = static_cast<size_t>(a.N) * E;
+          float s = 0.f;
+          int ks = 0;
+          for (; ks + 8 <= a.ksplit; ks += 8) {
+            float t8[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (valid[q]) m = fmaxf(m, l[q]);
-  m = wave_max_f32(m);
-  double zs = 0.0;
+            for (int u = 0; u < 8; ++u) t8[u] = p[(ks + u) * stride];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
-  const double z = wave_sum_f64(zs);
-
-  uint64_t key[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) key[q] = valid[q] ? topk_key(l[q], lane + kWave * q) : 0ull;
-  int my_nat = 0;  // lane j keeps the j-th natural expert
-  uint32_t in_nat = 0;  // bit q: slot q is in the natural top-k
-  for (int j = 0; j < k; ++j) {
-    uint64_t b = key[0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
-    b = wave_max_u64(b);
-    const int ew = b ? key_expert(b) : 0;
-    if ((ew & (kWave - 1)) == lane) {
-      const int q = ew >> 6;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        if (qq == q) {
-          key[qq] = 0ull;
-          in_nat |= 1u << qq;
+            for (int u = 0; u < 8; ++u) s += t8[u];
+          }
+          for (; ks < a.ksplit; ++ks) s += p[ks * stride];
+          v = s + (a.b_router ? a.b_router[e] : 0.f);
         }
+        a.logits[static_cast<size_t>(i) * E + e] = v;
+        if (a.logits_out) a.logits_out[static_cast<size_t>(i) * E + e] = v;
+        if (!isfinite(v)) nonfinite = true;
+      }
+      l[q] = v;
     }
-    if (lane == j) my_nat = ew;
-  }
-  if (lane < k) a.nat[static_cast<size_t>(i) * k + lane] = my_nat;
-
-  int d = a.depth[i];
-  const int dc = d < 0 ? 0 : (d >= a.n_depth ? a.n_depth - 1 : d);
-  const double c = static_cast<double>(a.commit[dc]);
+    float m = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (!valid[q]) continue;
-    const int e = lane + kWave * q;
-    double t = 0.0;
-    if (in_nat & (1u << q)) t = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
-    a.contrib[static_cast<size_t>(i) * E + e] = t;
-  }
-  const bool any_nf = __ballot(nonfinite) != 0ull;
-  if (lane == 0) {
-    int err = any_nf ? kErrNonFinite : 0;
-    const int p = a.parent[i];
-    if (d < 0 || d >= a.n_depth) err |= kErrDepth;
-    if (p == -1) {
-      if (d != 0) err |= kErrBadTree;
-    } else if (p < 0 || p >= i) {
-      err |= kErrBadTree;
-    } else if (d != a.depth[p] + 1) {
-      err |= kErrBadTree;
+    for (int q = 0; q < 4; ++q)
+      if (valid[q]) m = fmaxf(m, l[q]);
+    m = wave_max_f32(m);
+    double zs = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
+    const double z = wave_sum_f64(zs);
+
+    uint64_t key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) key[q] = valid[q] ? topk_key(l[q], lane + kWave * q) : 0ull;
+    int my_nat = 0;       // lane j keeps the j-th natural expert
+    uint32_t in_nat = 0;  // bit q: slot q is in the natural top-k
+    for (int j = 0; j < k; ++j) {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
+      b = wave_max_u64(b);
+      const int ew = b ? key_expert(b) : 0;
+      if ((ew & (kWave - 1)) == lane) {
+        const int q = ew >> 6;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qq == q) {
+            key[qq] = 0ull;
+            in_nat |= 1u << qq;
+          }
+      }
+      if (lane == j) my_nat = ew;
     }
-    a.node_err[i] = err;
-    a.node_m[i] = m;
-    a.node_z[i] = z;
+    if (lane < k) a.nat[static_cast<size_t>(i) * k + lane] = my_nat;
+
+    const int d = a.depth[i];
+    const int dc = d < 0 ? 0 : (d >= a.n_depth ? a.n_depth - 1 : d);
+    const double c = static_cast<double>(a.commit[dc]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!valid[q]) continue;
+      const int e = lane + kWave * q;
+      double t = 0.0;
+      if (in_nat & (1u << q)) t = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
+      a.contrib[static_cast<size_t>(i) * E + e] = t;
+    }
+    const bool any_nf = __ballot(nonfinite) != 0ull;
+    if (lane == 0) {
+      int err = any_nf ? kErrNonFinite : 0;
+      const int p = a.parent[i];
+      if (d < 0 || d >= a.n_depth) err |= kErrDepth;
+      if (p == -1) {
+        if (d != 0) err |= kErrBadTree;
+      } else if (p < 0 || p >= i) {
+        err |= kErrBadTree;
+      } else if (d != a.depth[p] + 1) {
+        err |= kErrBadTree;
+      }
+      a.node_err[i] = err;
+      a.node_m[i] = m;
+      a.node_z[i] = z;
+    }
   }
+  if (last_block_done(&a.counters[0], gridDim.x)) select_set(a);
 }
 
-struct StatsDev {  // mirrors acceptmoe_stats
-  int32_t n_anchor, n_selfsize, n_eligible, n_pruned, n_active, n_active_nonresident,
-      n_natural_union, err_flags;
-  double r_eff, demand_total;
-};
-
-// one 1024-thread work-group
-__global__ __launch_bounds__(1024) void select_set_kernel(SelectArgs a) {
+__device__ void select_set(const SelectArgs& a) {
   __shared__ double s_part[1024];
   __shared__ double s_d[kMaxE];
   __shared__ int s_anchor[kMaxE], s_natused[kMaxE], s_rank[kMaxE], s_elig[kMaxE];
@@ -369,44 +388,50 @@ __global__ __launch_bounds__(1024) void select_set_kernel(SelectArgs a) {
   }
 }
 
-// one wave per node
-__global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
+// one wave per node, 16 nodes per work-group
+__global__ __launch_bounds__(1024) void restricted_kernel(SelectArgs a) {
   const int lane = lane_id();
-  const int i = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
-  if (i >= a.N) return;
-  const int E = a.E, k = a.k;
-  const float* row = a.logits + static_cast<size_t>(i) * E;
-  uint64_t key[4];
+  const int i = blockIdx.x * 16 + static_cast<int>(threadIdx.x >> 6);
+  if (i < a.N) {
+    const int E = a.E, k = a.k;
+    const float* row = a.logits + static_cast<size_t>(i) * E;
+    uint64_t key[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + kWave * q;
-    key[q] = (e < E && a.eligible[e]) ? topk_key(row[e], e) : 0ull;
-  }
-  int my_sel = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t b = key[0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
-    b = wave_max_u64(b);
-    const int ew = b ? key_expert(b) : 0;
-    if ((ew & (kWave - 1)) == lane) {
-      const int q = ew >> 6;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        if (qq == q) key[qq] = 0ull;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + kWave * q;
+      key[q] = (e < E && a.eligible[e]) ? topk_key(row[e], e) : 0ull;
     }
-    if (lane == j) my_sel = ew;
+    int my_sel = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
+      b = wave_max_u64(b);
+      const int ew = b ? key_expert(b) : 0;
+      if ((ew & (kWave - 1)) == lane) {
+        const int q = ew >> 6;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qq == q) key[qq] = 0ull;
+      }
+      if (lane == j) my_sel = ew;
+    }
+    const double m = static_cast<double>(a.node_m[i]);
+    const double z = a.node_z[i];
+    double p = 0.0;
+    if (lane < k) p = exp(static_cast<double>(row[my_sel]) - m) / z;
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += __shfl(p, j, kWave);
+    if (lane < k) {
+      const double g = (a.flags & kFlagNoRenorm) ? p : p / s;
+      a.topk_idx[static_cast<size_t>(i) * k + lane] = my_sel;
+      a.topk_gate[static_cast<size_t>(i) * k + lane] = static_cast<float>(g);
+    }
   }
-  const double m = static_cast<double>(a.node_m[i]);
-  const double z = a.node_z[i];
-  double p = 0.0;
-  if (lane < k) p = exp(static_cast<double>(row[my_sel]) - m) / z;
-  double s = 0.0;
-  for (int j = 0; j < k; ++j) s += __shfl(p, j, kWave);
-  if (lane < k) {
-    const double g = (a.flags & kFlagNoRenorm) ? p : p / s;
-    a.topk_idx[static_cast<size_t>(i) * k + lane] = my_sel;
-    a.topk_gate[static_cast<size_t>(i) * k + lane] = static_cast<float>(g);
+  if (a.counts) {
+    if (last_block_done(&a.counters[1], gridDim.x))
+      permute_block(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
+                    a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats));
   }
 }
 
@@ -424,21 +449,20 @@ void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) 
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  if (!(a.flags & kFlagLogitsIn)) {
-    dim3 grid((a.E + kRT - 1) / kRT, (a.N + kRT - 1) / kRT, a.ksplit);
-    if (a.act_bf16)
-      router_partial_kernel<uint16_t><<<grid, 256, 0, stream>>>(
-          static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w_router), a.N,
-          a.E, a.H, a.kslice, a.part);
-    else
-      router_partial_kernel<float><<<grid, 256, 0, stream>>>(
-          static_cast<const float*>(a.x), static_cast<const float*>(a.w_router), a.N, a.E,
-          a.H, a.kslice, a.part);
-  }
-  const int nb = (a.N + 3) / 4;
-  node_kernel<<<nb, 256, 0, stream>>>(a);
-  select_set_kernel<<<1, 1024, 0, stream>>>(a);
-  restricted_kernel<<<nb, 256, 0, stream>>>(a);
+  // with given logits the router only resets the arrival counter
+  const bool lin = (a.flags & kFlagLogitsIn) != 0;
+  const dim3 grid = lin ? dim3(1, 1, 1) : dim3((a.E + kRT - 1) / kRT, (a.N + kRT - 1) / kRT, a.ksplit);
+  if (a.act_bf16)
+    router_partial_kernel<uint16_t><<<grid, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w_router), a.N, a.E,
+        a.H, a.kslice, a.part, a.counters, !lin);
+  else
+    router_partial_kernel<float><<<grid, 256, 0, stream>>>(
+        static_cast<const float*>(a.x), static_cast<const float*>(a.w_router), a.N, a.E, a.H,
+        a.kslice, a.part, a.counters, !lin);
+  const int nb = (a.N + 15) / 16;
+  node_kernel<<<nb, 1024, 0, stream>>>(a);
+  restricted_kernel<<<nb, 1024, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -15,13 +15,28 @@ class VerifyLayer:
 
     weights: dict with w_router [E,H], b_router [E] or None, w13 [E,2,I,H],
     w2 [E,H,I], optional s13/s2 (FP8), optional w13_shared/w2_shared
-    (+ s13_shared/s2_shared).  All device tensors.
+    (+ s13_shared/s2_shared).  All device tensors, row-major.  With pack=True
+    (the default for BF16 / FP8 weights) the expert weights are reordered
+    once into the packed layout the kernels stream fastest; the row-major
+    tensors are then not referenced.
     """
 
-    def __init__(self, shape: L.Shape, weights: dict, device=None, debug_outputs: bool = True):
-        self.shape = shape
+    def __init__(self, shape: L.Shape, weights: dict, device=None, debug_outputs: bool = True,
+                 pack: Optional[bool] = None):
+        if pack is None:
+            pack = shape.w_dtype != L.F32
+        self.shape = L.Shape.from_buffer_copy(shape)
+        self.shape.w_layout = L.LAYOUT_PACKED if pack else L.LAYOUT_ROWMAJOR
+        shape = self.shape
         self.w = dict(weights)
         dev = torch.device(device or weights["w13"].device)
+        if pack:
+            E = shape.E
+            self.w["w13"], self.w["w2"] = L.pack_experts(shape, weights["w13"], weights["w2"], E)
+            if weights.get("w13_shared") is not None:
+                p13, p2 = L.pack_experts(shape, weights["w13_shared"][None],
+                                         weights["w2_shared"][None], 1)
+                self.w["w13_shared"], self.w["w2_shared"] = p13, p2
         self.device = dev
         N, H, E, k = shape.N, shape.H, shape.E, shape.k
         adt = torch.float32 if shape.act_dtype == L.F32 else torch.bfloat16

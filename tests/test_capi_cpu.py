@@ -94,11 +94,6 @@ def test_workspace_sizes_and_small_workspace(m):
 def test_null_pointers_rejected(m):
     lib = m.raw()
     s = _shape(m)
-    for i in range(8):
-        vals = [FAKE.value] * 8
-        vals[i] = None
-        if i == 0:
-            continue
     inp = m.Inputs(*([FAKE.value] * 16))
     inp.parent = None
     out = m.Outputs(*([FAKE.value] * 8))
@@ -126,11 +121,38 @@ def test_null_pointers_rejected(m):
     assert lib.moe_combine(64, 8, 100, 1, *([FAKE] * 5), None) == -1
     assert lib.moe_combine(64, 8, 2048, 1, None, FAKE, FAKE, None, FAKE, None) == -1
     G = [FAKE] * 10
-    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 0, 1, *G, FAKE, 1 << 40, None) == -2
-    assert lib.moe_grouped_swiglu(64, 8, 128, 2000, 768, 1, 1, *G, FAKE, 1 << 40, None) == -1
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 0, 1, 0, *G, FAKE, 1 << 40, None) == -2
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2000, 768, 1, 1, 0, *G, FAKE, 1 << 40, None) == -1
     G8 = [FAKE] * 3 + [None] + [FAKE] * 6
-    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 1, 2, *G8, FAKE, 1 << 40, None) == -1
-    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 1, 1, *G, FAKE, 10, None) == -1
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 1, 2, 0, *G8, FAKE, 1 << 40, None) == -1
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 1, 1, 0, *G, FAKE, 10, None) == -1
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 0, 0, 1, *G, FAKE, 1 << 40, None) == -2
+    assert lib.moe_grouped_swiglu(64, 8, 128, 2048, 768, 1, 1, 7, *G, FAKE, 1 << 40, None) == -2
+
+
+def test_packed_layout_rules(m):
+    """The packed layout: sizes, and the cases it does not support."""
+    lib = m.raw()
+    s = _shape(m, w_layout=1)
+    n13 = lib.acceptmoe_packed_size(C.byref(s), 0, 128)
+    n2 = lib.acceptmoe_packed_size(C.byref(s), 1, 128)
+    # same bytes as row-major (K = 2048 and 768 are whole 128-chunks)
+    assert n13 == 128 * 2 * 768 * 2048 * 2 and n2 == 128 * 2048 * 768 * 2
+    s_odd = _shape(m, H=2880, I=2880)        # reduction padded to 2944
+    assert lib.acceptmoe_packed_size(C.byref(s_odd), 0, 1) == 2 * 2880 * 2944 * 2
+    s8 = _shape(m, w_dtype=2, H=7168, I=2048)
+    assert lib.acceptmoe_packed_size(C.byref(s8), 1, 256) == 256 * 7168 * 2048
+    f32 = _shape(m, act_dtype=0, w_dtype=0, w_layout=1)
+    assert lib.acceptmoe_packed_size(C.byref(f32), 0, 1) == 0
+    inp = m.Inputs(*([FAKE.value] * 16))
+    out = m.Outputs(*([FAKE.value] * 8))
+    assert lib.verify_block(C.byref(f32), C.byref(inp), C.byref(out), FAKE, 1 << 40, None) == -2
+    bad = _shape(m, w_layout=5)
+    assert lib.verify_block(C.byref(bad), C.byref(inp), C.byref(out), FAKE, 1 << 40, None) == -2
+    assert lib.acceptmoe_pack_experts(C.byref(s), 0, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.acceptmoe_pack_experts(C.byref(s), 4, FAKE, None, FAKE, FAKE, None) == -1
+    assert lib.acceptmoe_pack_experts(C.byref(s), 4, None, None, None, None, None) == -1
+    assert lib.acceptmoe_pack_experts(C.byref(f32), 4, FAKE, FAKE, FAKE, FAKE, None) == -2
 
 
 def test_logits_in_requires_logits(m):

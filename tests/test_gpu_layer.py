@@ -22,13 +22,13 @@ from gpu_cases import (TOL, check_selection, expert_fn_from, make_weights, max_r
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(lib, cfg, b, w, flags=None):
+def run_layer(lib, cfg, b, w, flags=None, pack=None):
     d = upload_block(b)
     sh = shape_of(lib, cfg)
     if flags is not None:
         sh.flags = flags
     weights = dict(w_router=d["w_router"], b_router=d["b_router"], **w)
-    layer = lib.VerifyLayer(sh, weights)
+    layer = lib.VerifyLayer(sh, weights, pack=pack)
     out = layer.run(d["x"], d["parent"], d["depth"], d["commit"], resident=d["resident"])
     torch.cuda.synchronize()
     return {k: v.clone() for k, v in out.items()}, lib.decode_stats(out["stats"])
@@ -56,14 +56,17 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "rowmajor"])
 @pytest.mark.parametrize("name,over", SMALL)
-def test_layer_parity_small(lib, name, over):
+def test_layer_parity_small(lib, name, over, pack):
     cfg = W.CONFIGS[name].with_(**over)
+    if pack and cfg.w == "f32":
+        pytest.skip("the packed layout is for bf16 / fp8 weights")
     w = make_weights(cfg, device="cuda", gen_device="cpu")
     for seed in range(3):
-        say(f"layer small {name} {over} seed {seed}")
+        say(f"layer small {name} {over} pack={pack} seed {seed}")
         b = W.make_block(cfg, seed)
-        out, st = run_layer(lib, cfg, b, w)
+        out, st = run_layer(lib, cfg, b, w, pack=pack)
         lg = out["logits_out"].cpu().numpy()
         lref = O.router_logits(W.to_exact_f64(b.x), W.to_exact_f64(b.w_router),
                                None if b.b_router is None else b.b_router.numpy())
