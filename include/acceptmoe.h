@@ -132,7 +132,13 @@ typedef struct acceptmoe_stats {
  *   logits_out [N,E] fp32 or NULL    eligible [E] uint8 (1 = in S)
  *   topk_idx  [N,k] int32            topk_gate [N,k] fp32
  *   stats     one acceptmoe_stats (device)
- *   ws        workspace of at least acceptmoe_select_workspace_size(shape) bytes
+ *   ws        workspace of at least acceptmoe_select_workspace_size(shape) bytes,
+ *             device memory owned by the caller.  Its first 4 KiB hold the
+ *             kernels' arrival counters: zero-fill the workspace once before
+ *             its first use (hipMemset at allocation); every call leaves the
+ *             counters at zero again, so it needs no clearing between calls,
+ *             also when the shape changes.  Calls that share a workspace
+ *             must not overlap in time (same stream, or synchronised).
  * ------------------------------------------------------------------------- */
 size_t acceptmoe_select_workspace_size(const acceptmoe_shape* shape);
 int acceptmoe_select(const acceptmoe_shape* shape, const void* x, const void* w_router,
@@ -255,6 +261,9 @@ typedef struct acceptmoe_outputs { /* device pointers; only y is required */
   acceptmoe_stats* stats;    /* [1] */
 } acceptmoe_outputs;
 
+/* ws: at least acceptmoe_workspace_size(shape) bytes, zero-filled once before
+ * its first use and not shared by overlapping calls, as for acceptmoe_select
+ * (the select stage's counters sit at the same offsets). */
 size_t acceptmoe_workspace_size(const acceptmoe_shape* shape);
 int verify_block(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
                  const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -65,28 +65,100 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
 }
 
 // ----------------------------------------------------- wave reductions ----
-// xor butterflies: every lane ends with the same, bitwise identical result
+// Reductions over the 64 lanes with DPP moves inside each 16-lane row (xor 1,
+// xor 2, half-row mirror, row mirror) and one readlane per row.  Partner
+// values are combined commutatively, so every lane holds the same bits at
+// every step, and the four row results are combined in a fixed order: the
+// result is identical in all lanes and from run to run.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_mov<CTRL>(hi), ol = dpp_mov<CTRL>(lo);
+  const bool t = oh > hi || (oh == hi && ol > lo);
+  hi = t ? oh : hi;
+  lo = t ? ol : lo;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  max_step_u64<kDppXor1>(hi, lo);
+  max_step_u64<kDppXor2>(hi, lo);
+  max_step_u64<kDppHalfMirror>(hi, lo);
+  max_step_u64<kDppMirror>(hi, lo);
+  uint64_t r = 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, kWave);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
+  for (int row = 0; row < 4; ++row) {
+    const uint64_t o = (static_cast<uint64_t>(readlane_u32(hi, 16 * row)) << 32) |
+                       readlane_u32(lo, 16 * row);
+    r = o > r ? o : r;
   }
-  return v;
+  return r;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o = dpp_mov<kDppXor1>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<kDppXor2>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<kDppHalfMirror>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<kDppMirror>(v);
+  v = o > v ? o : v;
+  uint32_t r = readlane_u32(v, 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    const uint32_t x = readlane_u32(v, 16 * row);
+    r = x > r ? x : r;
+  }
+  return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_mov<CTRL>(__float_as_uint(v)));
+}
 __device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  float r = __uint_as_float(readlane_u32(__float_as_uint(v), 0));
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  for (int row = 1; row < 4; ++row) r = fmaxf(r, __uint_as_float(readlane_u32(__float_as_uint(v), 16 * row)));
+  return r;
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t o = (static_cast<uint64_t>(dpp_mov<CTRL>(static_cast<uint32_t>(u >> 32))) << 32) |
+                     dpp_mov<CTRL>(static_cast<uint32_t>(u));
+  return __builtin_bit_cast(double, o);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t o = (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(u >> 32), lane)) << 32) |
+                     readlane_u32(static_cast<uint32_t>(u), lane);
+  return __builtin_bit_cast(double, o);
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v = v + dpp_f64<kDppXor1>(v);
+  v = v + dpp_f64<kDppXor2>(v);
+  v = v + dpp_f64<kDppHalfMirror>(v);
+  v = v + dpp_f64<kDppMirror>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }

@@ -27,17 +27,20 @@ struct SelectArgs {
   float* topk_gate;
   void* stats;  // acceptmoe_stats*
   // workspace carve-up
-  float* part;       // [ksplit][N][E] router partial sums
+  float* part;         // [ksplit][N][E] router partial sums
   int ksplit;
   int kslice;
-  float* logits;     // [N][E]
-  float* node_m;     // [N]
-  double* node_z;    // [N]
-  int32_t* nat;      // [N][k]
-  double* contrib;   // [N][E]
-  int32_t* node_err; // [N]
-  int32_t* counters; // [2]: node-kernel and restricted-kernel arrival counters
-  // when non-null, the restricted kernel's last work-group also groups the
+  float* logits;       // [N][E]
+  float* node_m;       // [N] row max of the logits
+  double* node_z;      // [N] softmax denominator
+  int32_t* nat_idx;    // [N][k] natural top-k experts, slot order
+  float* nat_logit;    // [N][k] their logits
+  double* d_part;      // [N/4][E] demand summed over each node work-group's 4 nodes
+  uint8_t* f_part;     // [N/4][E] bit 0: a root routes to the expert, bit 1: some node does
+  int32_t* e_part;     // [N/4] error bits of each node work-group
+  int32_t* counters;   // [2]: group arrivals (front kernel), restricted-kernel arrivals
+  int32_t* gcount;     // [N/4]: K-slice arrivals per node group (zero between calls)
+  // when non-null, the restricted top-k is followed by the grouping of the
   // assignments by expert (moe_route_permute's outputs)
   int32_t* counts;
   int32_t* offsets;
@@ -47,10 +50,11 @@ struct SelectArgs {
   int32_t* n_active;
 };
 
-// router partial products, per-node softmax / natural top-k / demand terms,
-// set selection, restricted top-k and gates
+// router product, per-node softmax / natural top-k / demand terms, set
+// selection, restricted top-k, gates (and the grouping when counts is set)
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 void select_plan(int N, int H, int E, int num_cu, int* ksplit, int* kslice);
+int node_workgroups(int N);  // node groups of the front kernel (rows of d_part)
 
 // grouping of the N*k assignments by expert; resident/stats may be null
 hipError_t launch_permute(int N, int k, int E, const int32_t* topk_idx, int32_t* counts,

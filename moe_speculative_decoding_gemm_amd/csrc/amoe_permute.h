@@ -1,12 +1,12 @@
 // Group-by-expert of the N*k assignments [MoE-SD blog, MoE layer], as a
-// device function run by one 1024-thread work-group.
+// device function run by one work-group of 256 or 1024 threads.
 //
 // Pass 1 is an LDS histogram (integer atomics: the counts do not depend on
 // their order).  One wave scans the counts into offsets and compacts the
 // active experts.  Pass 2 scatters in rounds of 1024 assignments: inside a
 // wave, lanes with the same expert find each other with eight ballots over
 // the expert-id bits and take their rank from a popcount of the lower peers;
-// per-wave totals are scanned across the 16 waves in wave order.  Ranks
+// per-wave totals are scanned across the waves in wave order.  Ranks
 // follow assignment order, so the sort is stable and deterministic.
 #pragma once
 
@@ -50,64 +50,73 @@ __device__ __forceinline__ int wave_exclusive_scan_256(const int* v, int* out, i
   return __shfl(inc, kWave - 1, kWave);
 }
 
-// Requires blockDim.x == 1024.  An out-of-range expert id (a caller error)
-// is clamped so that no access leaves its buffer.
+// LDS of permute_block for NTHR threads
+template <int NTHR>
+struct PermuteSmem {
+  int cnt[kMaxE];
+  int off[kMaxE];
+  int flag[kMaxE];
+  int apos[kMaxE];
+  int run[kMaxE];
+  int w[NTHR / kWave][kMaxE];
+  int nact;
+};
+
+// Requires blockDim.x == NTHR (256 or 1024).  topk_idx may point to global
+// memory or to LDS.  An out-of-range expert id (a caller error) is clamped so
+// that no access leaves its buffer.
+template <int NTHR>
 __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t* topk_idx,
                                               int32_t* counts, int32_t* offsets,
                                               int32_t* sorted_assign, int32_t* inv_pos,
                                               int32_t* active, int32_t* n_active,
-                                              const uint8_t* resident, StatsDev* stats) {
-  __shared__ int s_cnt[kMaxE];
-  __shared__ int s_off[kMaxE];
-  __shared__ int s_flag[kMaxE];
-  __shared__ int s_apos[kMaxE];
-  __shared__ int s_run[kMaxE];
-  __shared__ int s_w[16][kMaxE];
-  __shared__ int s_nact;
+                                              const uint8_t* resident, StatsDev* stats,
+                                              PermuteSmem<NTHR>& sm) {
+  constexpr int NW = NTHR / kWave;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
   const int total = N * k;
   if (t < kMaxE) {
-    s_cnt[t] = 0;
-    s_run[t] = 0;
+    sm.cnt[t] = 0;
+    sm.run[t] = 0;
   }
   __syncthreads();
-  for (int x = t; x < total; x += 1024) atomicAdd(&s_cnt[clamp_expert(topk_idx[x], E)], 1);
+  for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
   __syncthreads();
-  if (t < E) s_flag[t] = s_cnt[t] > 0 ? 1 : 0;
+  if (t < E) sm.flag[t] = sm.cnt[t] > 0 ? 1 : 0;
   __syncthreads();
   if (wave == 0) {
-    wave_exclusive_scan_256(s_cnt, s_off, E);
-    const int na = wave_exclusive_scan_256(s_flag, s_apos, E);
-    if (lane == 0) s_nact = na;
+    wave_exclusive_scan_256(sm.cnt, sm.off, E);
+    const int na = wave_exclusive_scan_256(sm.flag, sm.apos, E);
+    if (lane == 0) sm.nact = na;
   }
   __syncthreads();
   if (t < E) {
-    counts[t] = s_cnt[t];
-    offsets[t] = s_off[t];
-    if (s_flag[t]) active[s_apos[t]] = t;
+    counts[t] = sm.cnt[t];
+    offsets[t] = sm.off[t];
+    if (sm.flag[t]) active[sm.apos[t]] = t;
   }
   if (t == 0) {
     offsets[E] = total;
-    n_active[0] = s_nact;
+    n_active[0] = sm.nact;
   }
   if (stats && t < kWave) {
     int nr = 0;
     if (resident)
-      for (int e = t; e < E; e += kWave) nr += (s_flag[e] && !resident[e]) ? 1 : 0;
+      for (int e = t; e < E; e += kWave) nr += (sm.flag[e] && !resident[e]) ? 1 : 0;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) nr += __shfl_xor(nr, m, kWave);
     if (t == 0) {
-      stats->n_active = s_nact;
+      stats->n_active = sm.nact;
       stats->n_active_nonresident = nr;
     }
   }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = 0; base < total; base += 1024) {
+  for (int base = 0; base < total; base += NTHR) {
     const int x = base + t;
     const bool valid = x < total;
     const int e = valid ? clamp_expert(topk_idx[x], E) : 0;
-    for (int q = lane; q < E; q += kWave) s_w[wave][q] = 0;
+    for (int q = lane; q < E; q += kWave) sm.w[wave][q] = 0;
     const uint64_t vmask = __ballot(valid);
     uint64_t peers = vmask;
 #pragma unroll
@@ -117,21 +126,21 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
       peers &= bit ? mb : ~mb;
     }
     const int rank = __popcll(peers & below);
-    if (valid && rank == 0) s_w[wave][e] = __popcll(peers);
+    if (valid && rank == 0) sm.w[wave][e] = __popcll(peers);
     __syncthreads();
     if (t < E) {
-      int run = s_run[t];
+      int run = sm.run[t];
 #pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int c = s_w[w][t];
-        s_w[w][t] = run;
+      for (int w = 0; w < NW; ++w) {
+        const int c = sm.w[w][t];
+        sm.w[w][t] = run;
         run += c;
       }
-      s_run[t] = run;
+      sm.run[t] = run;
     }
     __syncthreads();
     if (valid) {
-      const int pos = s_off[e] + s_w[wave][e] + rank;
+      const int pos = sm.off[e] + sm.w[wave][e] + rank;
       sorted_assign[pos] = x;
       inv_pos[x] = pos;
     }
@@ -142,20 +151,29 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
 // Last-arriver election: every thread of the work-group calls this after its
 // global writes.  Returns true in exactly one work-group of the grid -- the
 // last to arrive -- after which that work-group sees every other
-// work-group's writes.  The counter must be zero at kernel start; the
-// caller's previous kernel in stream order resets it.
+// work-group's writes.  The barrier completes the writes of all waves at
+// work-group scope; one thread then makes them visible at device scope
+// (release) before it counts the arrival, and the last arriver's thread
+// acquires before the second barrier.  One device-scope fence per
+// work-group, not one per wave: each such fence writes back the L2 of its
+// XCD, and many of them in flight serialise.  The counter must be zero at
+// kernel start; the last work-group resets it, so it stays zero between
+// launches.
 __device__ __forceinline__ bool last_block_done(int* counter, int nblocks) {
   __shared__ int s_last;
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
+    __threadfence();
     const int prev = atomicAdd(counter, 1);
-    s_last = prev == nblocks - 1;
+    const bool last = prev == nblocks - 1;
+    if (last) {
+      __threadfence();
+      *counter = 0;  // ready for the next launch
+    }
+    s_last = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
 }
 
 }  // namespace amoe

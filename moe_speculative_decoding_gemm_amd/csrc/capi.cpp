@@ -110,25 +110,34 @@ struct SelectWs {
   float* logits;
   float* node_m;
   double* node_z;
-  int32_t* nat;
-  double* contrib;
-  int32_t* node_err;
+  int32_t* nat_idx;
+  float* nat_logit;
+  double* d_part;
+  uint8_t* f_part;
+  int32_t* e_part;
   int32_t* counters;
+  int32_t* gcount;
   int ksplit, kslice;
 };
 
 SelectWs carve_select(Carver& c, const acceptmoe_shape* s) {
   SelectWs w;
   amoe::select_plan(s->N, s->H, s->E, 0, &w.ksplit, &w.kslice);
+  // arrival counters first, at offsets that do not depend on the shape: the
+  // kernels leave them at zero, so a zero-filled workspace stays valid
+  w.counters = c.take<int32_t>(2);
+  w.gcount = c.take<int32_t>(4096 / 4);
   const size_t NE = static_cast<size_t>(s->N) * s->E;
   w.part = c.take<float>(static_cast<size_t>(w.ksplit) * NE);
   w.logits = c.take<float>(NE);
   w.node_m = c.take<float>(s->N);
   w.node_z = c.take<double>(s->N);
-  w.nat = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
-  w.contrib = c.take<double>(NE);
-  w.node_err = c.take<int32_t>(s->N);
-  w.counters = c.take<int32_t>(2);
+  w.nat_idx = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
+  w.nat_logit = c.take<float>(static_cast<size_t>(s->N) * s->k);
+  const size_t nwg = amoe::node_workgroups(s->N);
+  w.d_part = c.take<double>(nwg * s->E);
+  w.f_part = c.take<uint8_t>(nwg * s->E);
+  w.e_part = c.take<int32_t>(nwg);
   return w;
 }
 
@@ -211,10 +220,13 @@ amoe::SelectArgs select_args(const acceptmoe_shape* s, const SelectWs& w) {
   a.logits = w.logits;
   a.node_m = w.node_m;
   a.node_z = w.node_z;
-  a.nat = w.nat;
-  a.contrib = w.contrib;
-  a.node_err = w.node_err;
+  a.nat_idx = w.nat_idx;
+  a.nat_logit = w.nat_logit;
+  a.d_part = w.d_part;
+  a.f_part = w.f_part;
+  a.e_part = w.e_part;
   a.counters = w.counters;
+  a.gcount = w.gcount;
   return a;
 }
 
@@ -457,7 +469,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.topk_idx = topk_idx;
   a.topk_gate = topk_gate;
   a.stats = stats;
-  // the restricted top-k kernel's last work-group also groups by expert
+  // the selection stage also groups the assignments by expert
   a.counts = counts;
   a.offsets = w.offsets;
   a.sorted_assign = w.sorted_assign;

@@ -20,8 +20,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(int N, int k, int E,
                                                        int32_t* __restrict__ n_active,
                                                        const uint8_t* __restrict__ resident,
                                                        StatsDev* __restrict__ stats) {
-  permute_block(N, k, E, topk_idx, counts, offsets, sorted_assign, inv_pos, active, n_active,
-                resident, stats);
+  __shared__ PermuteSmem<1024> sm;
+  permute_block<1024>(N, k, E, topk_idx, counts, offsets, sorted_assign, inv_pos, active,
+                      n_active, resident, stats, sm);
 }
 
 __global__ void shared_grouping_kernel(int N, int32_t* offsets, int32_t* sorted_assign,

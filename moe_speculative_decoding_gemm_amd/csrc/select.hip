@@ -1,30 +1,36 @@
 // AcceptMoE expert selection on gfx950: router product, per-node softmax and
 // natural top-k, commitment-weighted demand, anchor, self-sizing,
-// residency-aware pruning, restricted top-k and gates.
+// residency-aware pruning, restricted top-k, gates and the grouping of the
+// assignments by expert.
 //
 // Sources: [MoE-SD blog, MoE layer] for the router (softmax over all experts,
-// top-k routing); [AcceptMoE news §02] and [AcceptMoE abstract] for demand,
-// root anchor, self-sizing by effective rank and residency-aware pruning;
-// [AcceptMoE abstract] for restricting top-k to the eligible set.
+// top-k routing) and the grouping; [AcceptMoE news §02] and [AcceptMoE
+// abstract] for demand, root anchor, self-sizing by effective rank and
+// residency-aware pruning; [AcceptMoE abstract] for restricting top-k to the
+// eligible set.
 //
-// Three kernels, all wave64:
-//   router_partial  grid (E/64, N/64, ksplit): 64x64 logit tile over one K slice
-//                   per work-group, fp32 FMA from LDS (vector ALU: the router is
-//                   a few MFLOP at batch one; matrix cores are kept for the
-//                   expert contractions).
-//   node            one wave per node (16 per work-group): sum of the K-slice
-//                   partials + bias, fp64 softmax statistics, natural top-k by
-//                   64-bit (logit, ~index) keys, dense demand terms
-//                   c[depth] * p for the node's top-k.  The last work-group to
-//                   finish then selects the set: demand per expert (fixed
-//                   summation order), entropy, set size, anchor + fill by rank
-//                   counting, pruning by rank counting, statistics.
-//   restricted      one wave per node: top-k over the eligible experts and the
-//                   gates; the last work-group to finish groups the
-//                   assignments by expert (verify_block only).
-// Arrival counters are reset by the kernel before, in stream order, so no
-// memset is needed.  Every reduction has a fixed order: two runs give
-// identical bits.
+// One kernel (front_kernel, wave64, 256 threads per work-group) over a grid of
+// (node groups of 4) x (K slices of the router product):
+//   router   each work-group: the 4 nodes' logits over its K slice for all
+//            experts, fp32 FMAs with x in LDS (vector ALU: the router is a few
+//            MFLOP per block; the matrix cores are kept for the experts).
+//   node     the last K-slice work-group of a group to finish: one wave per
+//            node sums the slice partials (+ bias), takes fp64 softmax
+//            statistics and the natural top-k by 64-bit (logit, ~index) keys,
+//            and adds the demand terms c[depth] * p of the node's top-k into
+//            one partial row per group.
+//   tail     the last group to finish: demand per expert (fixed summation
+//            order), entropy, set size, anchor + fill and pruning by rank
+//            counting; then (N <= kFusedMaxN) every node's restricted top-k,
+//            the gates and the grouping by expert.  A node whose natural
+//            top-k lies inside the set keeps it (the k largest keys of all
+//            experts are the k largest of any superset of them); the others
+//            rank their set members' keys by counting.
+// For N > kFusedMaxN a second kernel (restricted_kernel, one wave per node)
+// takes the restricted top-k and gates, and its last work-group groups.
+// Every reduction has a fixed order: two runs give identical bits.  Arrival
+// counters are left at zero by the last arriver, so a zero-filled workspace
+// stays valid across calls.
 
 #include "amoe_common.h"
 #include "amoe_launch.h"
@@ -34,345 +40,380 @@ namespace amoe {
 
 namespace {
 
-constexpr int kRT = 64;   // router tile (tokens and experts)
-constexpr int kRKC = 32;  // router K chunk staged in LDS
+constexpr int kMaxKSplit = 16;   // router K slices (partial sums per logit)
+constexpr int kNodesPerWG = 4;   // nodes per group (one wave each in the node phase)
+constexpr int kMaxSlice = 2048;  // K elements per router slice
+constexpr int kFusedMaxN = 256;  // largest N whose restricted top-k runs in the tail
+constexpr int kKeyCap = 4096;    // (node, member) keys per rank-counting pass
+constexpr int kLgCap = 8192;     // logits the tail holds in LDS (N * E up to this)
 
+// MFMA operand fragment: 8 consecutive K elements of one row (x or W_r).
+// v_mfma_f32_16x16x32_bf16: A[m][kk] in lane m + 16g for kk in [8g, 8g+8),
+// B[kk][n] likewise in lane n + 16g, D[m][n] in lane n + 16g for m in
+// [4g, 4g+4).  fp32 inputs take eight v_mfma_f32_16x16x4_f32, MFMA i over the
+// elements 8g + i of each lane: together the same 16x16x32 product.
 template <typename AT>
-__device__ __forceinline__ void load8(const AT* p, float* out);
+struct RFrag;
 template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* out) {
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(v[i] << 16);
-    out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
-  }
-}
+struct RFrag<uint16_t> {
+  bf16x8_t v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8_t*>(p); }
+  __device__ __forceinline__ void zero() { v = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u}); }
+};
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* out) {
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[i] = a[i];
-    out[4 + i] = b[i];
+struct RFrag<float> {
+  f32x4_t lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const f32x4_t*>(p);
+    hi = *reinterpret_cast<const f32x4_t*>(p + 4);
   }
+  __device__ __forceinline__ void zero() {
+    lo = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    hi = lo;
+  }
+};
+__device__ __forceinline__ f32x4_t rmma(const RFrag<uint16_t>& a, const RFrag<uint16_t>& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
-
-// logits partial sums over one K slice: part[ks][n][e] = sum_k x[n][k] w[e][k]
+__device__ __forceinline__ f32x4_t rmma(const RFrag<float>& a, const RFrag<float>& b, f32x4_t c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[i], b.lo[i], c, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[i], b.hi[i], c, 0, 0, 0);
+  return c;
+}
+// K steps (32 wide) whose loads are issued together (a 256-long slice at
+// once for bf16): up to 128 VGPRs of W_r
 template <typename AT>
-__global__ __launch_bounds__(256) void router_partial_kernel(const AT* __restrict__ x,
-                                                             const AT* __restrict__ w, int N,
-                                                             int E, int H, int kslice,
-                                                             float* __restrict__ part,
-                                                             int32_t* __restrict__ counters,
-                                                             int compute) {
-  __shared__ float xs[kRKC][kRT + 4];
-  __shared__ float wsm[kRKC][kRT + 4];
-  const int t = threadIdx.x;
-  if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) counters[0] = 0;
-  if (!compute) return;
-  const int e0 = blockIdx.x * kRT, n0 = blockIdx.y * kRT, ks = blockIdx.z;
-  const int kbeg = ks * kslice;
-  const int kend = min(H, kbeg + kslice);
-  const int ty = t >> 4, tx = t & 15;
-  const int lr = t >> 2, lk = (t & 3) * 8;
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+struct RouterSteps {
+  static constexpr int n = sizeof(AT) == 2 ? 8 : 4;
+};
 
-  for (int kb = kbeg; kb < kend; kb += kRKC) {
-    float v[8];
-    const int n = n0 + lr;
-    if (n < N) {
-      load8<AT>(x + static_cast<size_t>(n) * H + kb + lk, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xs[lk + i][lr] = v[i];
-    const int e = e0 + lr;
-    if (e < E) {
-      load8<AT>(w + static_cast<size_t>(e) * H + kb + lk, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wsm[lk + i][lr] = v[i];
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kRKC; ++kk) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&xs[kk][ty * 4]);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&wsm[kk][tx * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + ty * 4 + i;
-    if (n >= N) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) part[(static_cast<size_t>(ks) * N + n) * E + e] = acc[i][j];
-    }
-  }
+// ------------------------------------------------------------------ LDS ----
+struct NodeSmem {
+  double c[kNodesPerWG][kMaxE];  // demand terms per node
+  int flags[kMaxE];              // bit 0: a root routes here, bit 1: some node does
+  int err;
+};
+struct SetSmem {
+  double d[kMaxE];
+  double key[kMaxE];
+  int anchor[kMaxE], rank[kMaxE], elig[kMaxE];
+  int err, na, nnat, nsel, ncand;
+  double tot, h;
+};
+struct TailSmem {
+  SetSmem set;
+  int member[kMaxE];  // eligible experts, ascending
+  int nmem;
+  int needy[kFusedMaxN];  // nodes whose natural top-k leaves the set
+  int nneedy;
+  int bad[kFusedMaxN];  // 1: the node's natural top-k leaves the set
+  float m[kFusedMaxN];
+  double z[kFusedMaxN];
+  float lg[kLgCap];                 // [node][expert] logits when N * E <= kLgCap
+  int top_e[kFusedMaxN * kMaxK];    // [node][slot] expert
+  float top_l[kFusedMaxN * kMaxK];  // [node][slot] logit
+  union {
+    uint64_t keys[kKeyCap];           // rank counting
+    double p[kFusedMaxN * kMaxK];     // gate numerators
+    PermuteSmem<256> perm;
+  } u;
+};
+union FrontSmem {
+  NodeSmem n;
+  TailSmem t;
+};
+
+// 32-bit order key of a logit: unsigned order = float order (-0 folded onto
+// +0), at least 1 so that 0 can mark an empty slot.  The 64-bit topk_key is
+// this key (unclamped) over ~index.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0u) u = 0u;
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return o > 1u ? o : 1u;
+}
+// an order key (or the high word of a topk_key) back to its logit
+__device__ __forceinline__ float order_logit(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  return order_logit(static_cast<uint32_t>(key >> 32));
 }
 
-// set selection by one 1024-thread work-group (the last node work-group)
-__device__ void select_set(const SelectArgs& a);
-
-// one wave per node, 16 nodes per work-group
-__global__ __launch_bounds__(1024) void node_kernel(SelectArgs a) {
+// ---------------------------------------------------------- node phase ----
+// Node i on one wave: logits from the K-slice partials (+ bias) or from
+// logits_in, fp64 softmax statistics, natural top-k (written in slot order),
+// demand terms into sm.c[slot], anchor / natural-use flags, error bits.
+// d, p, dp, cf: depth, parent, parent's depth and commit[depth] of node i.
+__device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot, NodeSmem& sm,
+                                           int d, int p, int dp, float cf, const float* bias) {
   const int lane = lane_id();
-  const int i = blockIdx.x * 16 + static_cast<int>(threadIdx.x >> 6);
-  if (threadIdx.x == 0 && blockIdx.x == 0) a.counters[1] = 0;
-  if (i < a.N) {
-    const int E = a.E, k = a.k;
-    const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
-    float l[4];
-    bool valid[4];
-    bool nonfinite = false;
+  const int E = a.E, k = a.k;
+  const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
+  float l[4];
+  bool valid[4];
+  bool nonfinite = false;
+  if (logits_in) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + kWave * q;
       valid[q] = e < E;
-      float v = 0.f;
-      if (valid[q]) {
-        if (logits_in) {
-          v = a.logits_in[static_cast<size_t>(i) * E + e];
-        } else {
-          // partial sums in K-slice order; loads issued eight at a time
-          const float* p = a.part + static_cast<size_t>(i) * E + e;
-          const size_t stride = static_cast<size_t>(a.N) * E;
-          float s = 0.f;
-          int ks = 0;
-          for (; ks + 8 <= a.ksplit; ks += 8) {
-            float t8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) t8[u] = p[(ks + u) * stride];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s += t8[u];
-          }
-          for (; ks < a.ksplit; ++ks) s += p[ks * stride];
-          v = s + (a.b_router ? a.b_router[e] : 0.f);
-        }
-        a.logits[static_cast<size_t>(i) * E + e] = v;
-        if (a.logits_out) a.logits_out[static_cast<size_t>(i) * E + e] = v;
-        if (!isfinite(v)) nonfinite = true;
-      }
-      l[q] = v;
+      l[q] = valid[q] ? a.logits_in[static_cast<size_t>(i) * E + e] : 0.f;
     }
-    float m = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (valid[q]) m = fmaxf(m, l[q]);
-    m = wave_max_f32(m);
-    double zs = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
-    const double z = wave_sum_f64(zs);
-
-    uint64_t key[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) key[q] = valid[q] ? topk_key(l[q], lane + kWave * q) : 0ull;
-    int my_nat = 0;       // lane j keeps the j-th natural expert
-    uint32_t in_nat = 0;  // bit q: slot q is in the natural top-k
-    for (int j = 0; j < k; ++j) {
-      uint64_t b = key[0];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
-      b = wave_max_u64(b);
-      const int ew = b ? key_expert(b) : 0;
-      if ((ew & (kWave - 1)) == lane) {
-        const int q = ew >> 6;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          if (qq == q) {
-            key[qq] = 0ull;
-            in_nat |= 1u << qq;
-          }
-      }
-      if (lane == j) my_nat = ew;
-    }
-    if (lane < k) a.nat[static_cast<size_t>(i) * k + lane] = my_nat;
-
-    const int d = a.depth[i];
-    const int dc = d < 0 ? 0 : (d >= a.n_depth ? a.n_depth - 1 : d);
-    const double c = static_cast<double>(a.commit[dc]);
+  } else {
+    // K-slice partial sums: every load issued first, then summed in slice order
+    const size_t stride = static_cast<size_t>(a.N) * E;
+    float pv[4][kMaxKSplit];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (!valid[q]) continue;
       const int e = lane + kWave * q;
-      double t = 0.0;
-      if (in_nat & (1u << q)) t = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
-      a.contrib[static_cast<size_t>(i) * E + e] = t;
+      valid[q] = e < E;
+      const float* pp = a.part + static_cast<size_t>(i) * E + e;
+#pragma unroll
+      for (int s = 0; s < kMaxKSplit; ++s)
+        if (valid[q] && s < a.ksplit) pv[q][s] = pp[s * stride];
     }
-    const bool any_nf = __ballot(nonfinite) != 0ull;
-    if (lane == 0) {
-      int err = any_nf ? kErrNonFinite : 0;
-      const int p = a.parent[i];
-      if (d < 0 || d >= a.n_depth) err |= kErrDepth;
-      if (p == -1) {
-        if (d != 0) err |= kErrBadTree;
-      } else if (p < 0 || p >= i) {
-        err |= kErrBadTree;
-      } else if (d != a.depth[p] + 1) {
-        err |= kErrBadTree;
-      }
-      a.node_err[i] = err;
-      a.node_m[i] = m;
-      a.node_z[i] = z;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float sum = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxKSplit; ++s)
+        if (valid[q] && s < a.ksplit) sum += pv[q][s];
+      l[q] = valid[q] ? sum + bias[q] : 0.f;
     }
   }
-  if (last_block_done(&a.counters[0], gridDim.x)) select_set(a);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (valid[q]) {
+      const int e = lane + kWave * q;
+      a.logits[static_cast<size_t>(i) * E + e] = l[q];
+      if (a.logits_out) a.logits_out[static_cast<size_t>(i) * E + e] = l[q];
+      if (!isfinite(l[q])) nonfinite = true;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (valid[q]) m = fmaxf(m, l[q]);
+  m = wave_max_f32(m);
+  double zs = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
+  const double z = wave_sum_f64(zs);
+
+  // natural top-k: k rounds of a wave max over 32-bit order keys; among equal
+  // keys the lowest expert index (slot q, then lane) wins
+  uint32_t key[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) key[q] = valid[q] ? order_key(l[q]) : 0u;
+  uint32_t in_nat = 0;  // bit q: slot q is in the natural top-k
+  int my_e = 0;         // lane j: expert of rank j
+  uint32_t my_o = 0;    //         and its key
+  for (int j = 0; j < k; ++j) {
+    uint32_t b = key[0] > key[1] ? key[0] : key[1];
+    const uint32_t b2 = key[2] > key[3] ? key[2] : key[3];
+    b = wave_max_u32(b > b2 ? b : b2);
+    const uint64_t m0 = __ballot(key[0] == b), m1 = __ballot(key[1] == b);
+    const uint64_t m2 = __ballot(key[2] == b), m3 = __ballot(key[3] == b);
+    const int qw = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : 3));
+    const uint64_t mw = m0 ? m0 : (m1 ? m1 : (m2 ? m2 : m3));
+    const int lw = static_cast<int>(__builtin_ctzll(mw));
+    if (lane == lw) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == qw) {
+          key[q] = 0u;
+          in_nat |= 1u << q;
+        }
+    }
+    if (lane == j) {
+      my_e = kWave * qw + lw;
+      my_o = b;
+    }
+  }
+  if (lane < k) {
+    a.nat_idx[static_cast<size_t>(i) * k + lane] = my_e;
+    a.nat_logit[static_cast<size_t>(i) * k + lane] = order_logit(my_o);
+  }
+  const double c = static_cast<double>(cf);
+  const int fl = p == -1 ? 3 : 2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (in_nat & (1u << q)) {
+      const int e = lane + kWave * q;
+      sm.c[slot][e] = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
+      atomicOr(&sm.flags[e], fl);
+    }
+  }
+  const bool any_nf = __ballot(nonfinite) != 0ull;
+  if (lane == 0) {
+    int err = any_nf ? kErrNonFinite : 0;
+    if (d < 0 || d >= a.n_depth) err |= kErrDepth;
+    if (p == -1) {
+      if (d != 0) err |= kErrBadTree;
+    } else if (p < 0 || p >= i) {
+      err |= kErrBadTree;
+    } else if (d != dp + 1) {
+      err |= kErrBadTree;
+    }
+    if (err) atomicOr(&sm.err, err);
+    a.node_m[i] = m;
+    a.node_z[i] = z;
+  }
 }
 
-__device__ void select_set(const SelectArgs& a) {
-  __shared__ double s_part[1024];
-  __shared__ double s_d[kMaxE];
-  __shared__ int s_anchor[kMaxE], s_natused[kMaxE], s_rank[kMaxE], s_elig[kMaxE];
-  __shared__ int s_err, s_na, s_nnat, s_nsel, s_ncand;
-  __shared__ double s_tot, s_h;
+// ------------------------------------------------------- set selection ----
+// Rank of expert t among the experts by counting over key[0..EP), where key
+// holds the demand of the experts that take part and a sentinel for the rest
+// (below or above every demand, so it never counts).  desc: order (key desc,
+// index asc); else (key asc, index desc).  The E x EP comparisons are split
+// over the 256 threads: thread (e, part) counts over one part of the keys and
+// the parts are added in LDS.  Call with the whole work-group; returns the
+// rank in threads t < E with take[t] set.
+__device__ __forceinline__ int split_rank(const double* key, int* scratch, int E, bool desc,
+                                          const int* take) {
   const int t = threadIdx.x;
-  const int N = a.N, E = a.E, k = a.k;
-  const bool natural = (a.flags & kFlagNatural) != 0;
-  if (t < kMaxE) {
-    s_anchor[t] = 0;
-    s_natused[t] = 0;
-    s_rank[t] = 0;
-  }
-  if (t == 0) {
-    s_err = 0;
-    s_na = 0;
-    s_nnat = 0;
-    s_nsel = 0;
-    s_ncand = 0;
-  }
-  __syncthreads();
-  for (int i = t; i < N; i += 1024) {
-    const int e = a.node_err[i];
-    if (e) atomicOr(&s_err, e);
-  }
-  for (int d = t; d < a.n_depth; d += 1024) {
-    const float c = a.commit[d];
-    if (!(c >= 0.f) || isinf(c)) atomicOr(&s_err, kErrCommit);
-  }
-  for (int x = t; x < N * k; x += 1024) {
-    const int e = a.nat[x];
-    s_natused[e] = 1;
-    if (a.parent[x / k] == -1) s_anchor[e] = 1;
-  }
-  // demand: G groups of consecutive nodes, summed in group order
-  const int G = 1024 / E;
-  {
-    const int g = t / E, e = t - g * E;
-    double s = 0.0;
-    if (g < G) {
-      const int chunk = (N + G - 1) / G;
-      const int lo = g * chunk, hi = min(N, lo + chunk);
-      for (int i = lo; i < hi; ++i) s += a.contrib[static_cast<size_t>(i) * E + e];
+  const int EP = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  const int tpe = 256 / EP, e = t % EP, part = t / EP;
+  const int span = EP / tpe;  // a multiple of 16
+  int r = 0;
+  if (e < E && take[e]) {
+    const double de = key[e];
+    const int f0 = part * span;
+    for (int f = f0; f < f0 + span; f += 8) {
+      // eight keys read first, then compared without branches
+      double df[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) df[u] = key[f + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int strict = desc ? (df[u] > de) : (df[u] < de);
+        const int tie = (df[u] == de) & (desc ? (f + u < e) : (f + u > e));
+        r += strict | tie;
+      }
     }
-    s_part[t] = s;
+  }
+  scratch[part * EP + e] = r;
+  __syncthreads();
+  int rank = 0;
+  if (t < E)
+    for (int pp = 0; pp < tpe; ++pp) rank += scratch[pp * EP + t];
+  __syncthreads();
+  return rank;
+}
+
+// One 256-thread work-group.  nwg partial rows of demand / flags / errors.
+// Leaves the eligible flags in sm.elig (and in a.eligible), statistics in
+// a.stats (n_active is filled by the grouping).
+__device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
+  static_assert(kMaxE == 256, "select_set runs one thread per expert slot");
+  const int t = threadIdx.x;
+  const int E = a.E, k = a.k;
+  const bool natural = (a.flags & kFlagNatural) != 0;
+  if (t == 0) {
+    sm.err = 0;
+    sm.na = 0;
+    sm.nnat = 0;
+    sm.nsel = 0;
+    sm.ncand = 0;
   }
   __syncthreads();
+  // demand per expert: partial rows summed in group order
+  int f = 0;
+  double dsum = 0.0;
   if (t < E) {
-    double d = 0.0;
-    for (int g = 0; g < G; ++g) d += s_part[g * E + t];
-    s_d[t] = d;
-    if (s_anchor[t]) atomicAdd(&s_na, 1);
-    if (s_natused[t]) atomicAdd(&s_nnat, 1);
+    constexpr int B = 16;
+    for (int w0 = 0; w0 < nwg; w0 += B) {
+      double dv[B];
+      int fv[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (w0 + u < nwg) {
+          dv[u] = a.d_part[static_cast<size_t>(w0 + u) * E + t];
+          fv[u] = a.f_part[static_cast<size_t>(w0 + u) * E + t];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (w0 + u < nwg) {
+          dsum += dv[u];
+          f |= fv[u];
+        }
+      }
+    }
+    if (f & 1) atomicAdd(&sm.na, 1);
+    if (f & 2) atomicAdd(&sm.nnat, 1);
+  }
+  sm.d[t] = dsum;
+  sm.anchor[t] = f & 1;
+  for (int w = t; w < nwg; w += 256) {
+    const int e = a.e_part[w];
+    if (e) atomicOr(&sm.err, e);
+  }
+  for (int dd = t; dd < a.n_depth; dd += 256) {
+    const float c = a.commit[dd];
+    if (!(c >= 0.f) || isinf(c)) atomicOr(&sm.err, kErrCommit);
   }
   __syncthreads();
   if (t < kWave) {  // wave 0: total demand and entropy, fixed order
-    double s = 0.0;
-    for (int e = t; e < E; e += kWave) s += s_d[e];
-    const double tot = wave_sum_f64(s);
+    double sd = 0.0;
+    for (int e = t; e < E; e += kWave) sd += sm.d[e];
+    const double tot = wave_sum_f64(sd);
     double h = 0.0;
     if (tot > 0.0) {
       for (int e = t; e < E; e += kWave) {
-        const double d = s_d[e];
-        if (d > 0.0) {
-          const double q = d / tot;
+        const double dv = sm.d[e];
+        if (dv > 0.0) {
+          const double q = dv / tot;
           h -= q * log(q);
         }
       }
     }
     h = wave_sum_f64(h);
     if (t == 0) {
-      s_tot = tot;
-      s_h = h;
+      sm.tot = tot;
+      sm.h = h;
     }
   }
+  // fill order: (demand desc, index asc) over the non-anchor experts; anchors
+  // and padding carry demand -1, below every real demand
+  sm.key[t] = (t < E && !sm.anchor[t]) ? sm.d[t] : -1.0;
+  sm.elig[t] = t < E && !sm.anchor[t];  // experts that take part in the fill
   __syncthreads();
-  const double tot = s_tot;
-  const double r_eff = tot > 0.0 ? exp(s_h) : 0.0;
-  const int n_anchor = s_na;
+  const double tot = sm.tot;
+  const double r_eff = tot > 0.0 ? exp(sm.h) : 0.0;
+  const int n_anchor = sm.na;
   const int n_min = max(k, a.min_set);
   const int n_raw = a.fixed_budget > 0 ? a.fixed_budget : static_cast<int>(floor(r_eff + 0.5));
   const int n = min(E, max(max(n_raw, n_anchor), n_min));
   const int take = n - n_anchor;
-  // fill: rank of each non-anchor expert under (demand desc, index asc)
-  {
-    const int g = t / E, e = t - g * E;
-    if (g < G && !s_anchor[e]) {
-      const int chunk = (E + G - 1) / G;
-      const int lo = g * chunk, hi = min(E, lo + chunk);
-      const double de = s_d[e];
-      int r = 0;
-      for (int f = lo; f < hi; ++f)
-        if (!s_anchor[f] && (s_d[f] > de || (s_d[f] == de && f < e))) ++r;
-      if (r) atomicAdd(&s_rank[e], r);
-    }
-  }
-  __syncthreads();
+  const int fill_rank = split_rank(sm.key, sm.rank, E, true, sm.elig);
+  int el = 0;
   if (t < E) {
-    const int el = natural ? 1 : (s_anchor[t] || s_rank[t] < take) ? 1 : 0;
-    s_elig[t] = el;
-    if (el) atomicAdd(&s_nsel, 1);
+    el = natural ? 1 : (sm.anchor[t] || fill_rank < take) ? 1 : 0;
+    if (el) atomicAdd(&sm.nsel, 1);
   }
+  sm.elig[t] = el;
   __syncthreads();
-  const int n_selfsize = s_nsel;
+  const int n_selfsize = sm.nsel;
   int n_remove = 0;
   if (!natural && a.resident) {
-    if (t < E) {
-      s_rank[t] = 0;
-      const int cand = s_elig[t] && !s_anchor[t] && !a.resident[t];
-      if (cand) atomicAdd(&s_ncand, 1);
-    }
+    const bool cand = t < E && sm.elig[t] && !sm.anchor[t] && !a.resident[t];
+    if (cand) atomicAdd(&sm.ncand, 1);
+    // pruning order among candidates: demand ascending, index descending;
+    // non-candidates carry +infinity (never below a candidate's demand)
+    sm.key[t] = cand ? sm.d[t] : INFINITY;
+    sm.anchor[t] = cand;  // the anchor flags are no longer needed: candidates
     __syncthreads();
-    n_remove = max(0, min(a.reroute_budget, min(n_selfsize - n_min, s_ncand)));
-    // rank among candidates under (demand asc, index desc)
-    const int g = t / E, e = t - g * E;
-    const bool ce = (t < 1024) && g < G && s_elig[e] && !s_anchor[e] && !a.resident[e];
-    if (ce) {
-      const int chunk = (E + G - 1) / G;
-      const int lo = g * chunk, hi = min(E, lo + chunk);
-      const double de = s_d[e];
-      int r = 0;
-      for (int f = lo; f < hi; ++f) {
-        const bool cf = s_elig[f] && !s_anchor[f] && !a.resident[f];
-        if (cf && (s_d[f] < de || (s_d[f] == de && f > e))) ++r;
-      }
-      if (r) atomicAdd(&s_rank[e], r);
-    }
-    __syncthreads();
-    if (t < E) {
-      const bool c = s_elig[t] && !s_anchor[t] && !a.resident[t];
-      if (c && s_rank[t] < n_remove) s_elig[t] = 0;
-    }
+    n_remove = max(0, min(a.reroute_budget, min(n_selfsize - n_min, sm.ncand)));
+    const int prune_rank = split_rank(sm.key, sm.rank, E, false, sm.anchor);
+    if (cand && prune_rank < n_remove) sm.elig[t] = 0;
     __syncthreads();
   }
-  if (t < E) a.eligible[t] = static_cast<uint8_t>(s_elig[t]);
+  if (t < E) a.eligible[t] = static_cast<uint8_t>(sm.elig[t]);
   if (t == 0) {
     StatsDev* st = reinterpret_cast<StatsDev*>(a.stats);
     st->n_anchor = n_anchor;
@@ -381,17 +422,316 @@ __device__ void select_set(const SelectArgs& a) {
     st->n_pruned = n_remove;
     st->n_active = 0;
     st->n_active_nonresident = 0;
-    st->n_natural_union = s_nnat;
-    st->err_flags = s_err;
+    st->n_natural_union = sm.nnat;
+    st->err_flags = sm.err;
     st->r_eff = r_eff;
     st->demand_total = tot;
   }
 }
 
-// one wave per node, 16 nodes per work-group
-__global__ __launch_bounds__(1024) void restricted_kernel(SelectArgs a) {
+// ------------------------------------------------- restricted top-k tail ----
+// After select_set, by the same 256-thread work-group, for N <= kFusedMaxN,
+// with sm.top_e / top_l / m / z already holding the node phase's natural
+// top-k and softmax statistics: every node's top-k over the eligible set, the
+// gates, and (when a.counts is set) the grouping of the assignments by expert.
+// lg_lds: sm.lg holds the logits (else they are read from a.logits).
+__device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) {
+  const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+  const int N = a.N, E = a.E, k = a.k;
+  const int NK = N * k;
+  for (int i = t; i < N; i += 256) sm.bad[i] = 0;
+  if (wave == 0) {  // eligible experts in ascending order
+    const int nm = wave_exclusive_scan_256(sm.set.elig, sm.set.rank, kMaxE);
+    if (lane == 0) {
+      sm.nmem = nm;
+      sm.nneedy = 0;
+    }
+  }
+  __syncthreads();
+  if (t < E && sm.set.elig[t]) sm.member[sm.set.rank[t]] = t;
+  // nodes whose natural top-k leaves the set
+  for (int x = t; x < NK; x += 256)
+    if (!sm.set.elig[sm.top_e[x]]) sm.bad[x / k] = 1;
+  __syncthreads();
+  for (int i = t; i < N; i += 256)
+    if (sm.bad[i]) sm.needy[atomicAdd(&sm.nneedy, 1)] = i;
+  __syncthreads();
+  const int nm = sm.nmem, nneedy = sm.nneedy;
+  // rank counting over (needy node, member) keys, rows padded to a multiple
+  // of 4 with key 0 (below every key), as many nodes per pass as fit
+  const int nmp = (nm + 3) & ~3;
+  const int per = max(1, kKeyCap / max(nmp, 4));
+  const float inv = 1.0f / static_cast<float>(max(nmp, 1));
+  for (int c0 = 0; c0 < nneedy; c0 += per) {
+    const int cn = min(per, nneedy - c0);
+    const int total = cn * nmp;
+    for (int x = t; x < total; x += 256) {
+      int r = static_cast<int>(static_cast<float>(x) * inv);
+      if (r * nmp > x) --r;
+      if ((r + 1) * nmp <= x) ++r;
+      const int mm = x - r * nmp;
+      uint64_t key = 0ull;
+      if (mm < nm) {
+        const int i = sm.needy[c0 + r], e = sm.member[mm];
+        const float v = lg_lds ? sm.lg[i * E + e] : a.logits[static_cast<size_t>(i) * E + e];
+        key = topk_key(v, e);
+      }
+      sm.u.keys[x] = key;
+    }
+    __syncthreads();
+    for (int x = t; x < total; x += 256) {
+      int r = static_cast<int>(static_cast<float>(x) * inv);
+      if (r * nmp > x) --r;
+      if ((r + 1) * nmp <= x) ++r;
+      const uint64_t mine = sm.u.keys[x];
+      const uint64_t* row = &sm.u.keys[r * nmp];
+      int rank = 0;
+      int f = 0;
+      for (; f + 8 <= nmp; f += 8) {
+        uint64_t rf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rf[u] = row[f + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += static_cast<int>(rf[u] > mine);
+      }
+      if (f < nmp) {
+        uint64_t rf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rf[u] = row[f + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += static_cast<int>(rf[u] > mine);
+      }
+      if (mine != 0ull && rank < k) {
+        const int i = sm.needy[c0 + r];
+        sm.top_e[i * k + rank] = key_expert(mine);
+        sm.top_l[i * k + rank] = key_logit(mine);
+      }
+    }
+    __syncthreads();
+  }
+  // gates: fp64 softmax scores of the chosen experts, renormalised over the
+  // node's k slots in slot order
+  for (int x = t; x < NK; x += 256) {
+    const int i = x / k;
+    sm.u.p[x] = exp(static_cast<double>(sm.top_l[x]) - static_cast<double>(sm.m[i])) / sm.z[i];
+  }
+  __syncthreads();
+  const bool renorm = (a.flags & kFlagNoRenorm) == 0;
+  for (int x = t; x < NK; x += 256) {
+    const int i = x / k;
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += sm.u.p[i * k + j];
+    const double g = renorm ? sm.u.p[x] / s : sm.u.p[x];
+    a.topk_idx[x] = sm.top_e[x];
+    a.topk_gate[x] = static_cast<float>(g);
+  }
+  __syncthreads();
+  if (a.counts)
+    permute_block<256>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
+                       a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
+                       sm.u.perm);
+}
+
+// commit[depth] and the parent's depth of node `node` (of any wave: clamped
+// addresses, no branches; dp is 0 when p is not an earlier node)
+__device__ __forceinline__ void node_deps(const SelectArgs& a, int node, int d, int p, float& cf,
+                                          int& dp) {
+  const int dc = d < 0 ? 0 : (d >= a.n_depth ? a.n_depth - 1 : d);
+  const bool pin = p >= 0 && p < node;
+  cf = a.commit[dc];
+  const int pd = a.depth[pin ? p : 0];
+  dp = pin ? pd : 0;
+}
+
+// ------------------------------------------------------------ router ----
+// Partial logits of group g's 4 nodes over K slice ks, for all experts, into
+// a.part[ks][node][expert].  Wave w takes the 16-expert tiles w, w + 4, ...
+// (TPW of them); MFMA rows 0..3 are the nodes (rows 4..15 are zeros), columns
+// the tile's experts; rows 4..15 repeat rows 0..3 and are discarded.  Every
+// load is issued unconditionally from a clamped address (rows past E or N
+// repeat the last one and are discarded), so that all of them are in flight
+// together.  The node's dependent inputs (commit of
+// its depth, its parent's depth) are loaded once the product's loads are
+// out, so that they share the round trip.
+template <typename AT, int TPW>
+__device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int ks, int wave,
+                                                int lane, int node, int d, int p, float& cf,
+                                                int& dp) {
+  constexpr int S = RouterSteps<AT>::n;
+  const int N = a.N, E = a.E, H = a.H;
+  const int n0 = g * kNodesPerWG;
+  const int kbeg = ks * a.kslice;
+  const int nsteps = min(H - kbeg, a.kslice) >> 5;
+  const int mrow = lane & 15, kq = (lane >> 4) * 8;
+  // MFMA rows 4..15 repeat rows 0..3 (their D rows are never stored)
+  const AT* xrow = static_cast<const AT*>(a.x) +
+                   static_cast<size_t>(min(n0 + (mrow & (kNodesPerWG - 1)), N - 1)) * H + kbeg + kq;
+  const AT* wrow[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int e = min((wave + 4 * tt) * 16 + mrow, E - 1);
+    wrow[tt] = static_cast<const AT*>(a.w_router) + static_cast<size_t>(e) * H + kbeg + kq;
+  }
+  f32x4_t acc[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsteps; s0 += S) {
+    RFrag<AT> bf[TPW][S];
+    RFrag<AT> af[S];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int s = 0; s < S; ++s) bf[tt][s].load(wrow[tt] + 32 * min(s0 + s, nsteps - 1));
+#pragma unroll
+    for (int s = 0; s < S; ++s) af[s].load(xrow + 32 * min(s0 + s, nsteps - 1));
+    if (s0 == 0) {
+      asm volatile("" ::: "memory");
+      node_deps(a, node, d, p, cf, dp);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (s0 + s < nsteps) {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) acc[tt] = rmma(af[s], bf[tt][s], acc[tt]);
+      }
+  }
+  // D rows 0..3 (the nodes) sit in lanes 0..15, one expert column each
+  if (lane < 16) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int e = (wave + 4 * tt) * 16 + lane;
+      if (e < E) {
+#pragma unroll
+        for (int r = 0; r < kNodesPerWG; ++r)
+          if (n0 + r < N) a.part[(static_cast<size_t>(ks) * N + n0 + r) * E + e] = acc[tt][r];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- kernel ----
+template <typename AT, bool kFused>
+__global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
+  __shared__ __attribute__((aligned(16))) FrontSmem sm;
+  const int t = threadIdx.x, wave = t >> 6, lane = lane_id();
+  const int g = blockIdx.x, ks = blockIdx.y;
+  const int N = a.N, E = a.E, H = a.H;
+  const int n0 = g * kNodesPerWG;
+  const int node = n0 + wave;  // this wave's node in the node phase
+  const bool has_node = node < N;
+  const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
+
+  // node-phase inputs that do not depend on the logits, loaded up front (from
+  // clamped addresses, without branches) so that their latency hides under
+  // the router phase; the dependent ones follow once the product's loads are
+  // out
+  const int nd = min(node, N - 1);
+  const int d = a.depth[nd], p = a.parent[nd];
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.b_router) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bias[q] = a.b_router[min(lane + kWave * q, E - 1)];
+  }
+  float cf;
+  int dp;
+  if (!logits_in) {
+    // ---- partial logits of the group's 4 nodes over K slice ks
+    const int tpw = ((E + 15) / 16 + 3) / 4;  // 16-expert tiles per wave
+    if (tpw == 1)
+      router_partials<AT, 1>(a, g, ks, wave, lane, node, d, p, cf, dp);
+    else if (tpw == 2)
+      router_partials<AT, 2>(a, g, ks, wave, lane, node, d, p, cf, dp);
+    else if (tpw == 3)
+      router_partials<AT, 3>(a, g, ks, wave, lane, node, d, p, cf, dp);
+    else
+      router_partials<AT, 4>(a, g, ks, wave, lane, node, d, p, cf, dp);
+    if (!last_block_done(&a.gcount[g], gridDim.y)) return;
+  } else {
+    node_deps(a, node, d, p, cf, dp);
+  }
+
+  // ---- node phase (the group's last K-slice work-group)
+  for (int x = t; x < kMaxE; x += 256) {
+    sm.n.flags[x] = 0;
+#pragma unroll
+    for (int w = 0; w < kNodesPerWG; ++w) sm.n.c[w][x] = 0.0;
+  }
+  if (t == 0) sm.n.err = 0;
+  __syncthreads();
+  if (has_node) node_phase(a, node, wave, sm.n, d, p, dp, cf, bias);
+  __syncthreads();
+  for (int x = t; x < E; x += 256) {
+    double dsum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kNodesPerWG; ++w) dsum += sm.n.c[w][x];  // node order
+    a.d_part[static_cast<size_t>(g) * E + x] = dsum;
+    a.f_part[static_cast<size_t>(g) * E + x] = static_cast<uint8_t>(sm.n.flags[x]);
+  }
+  if (t == 0) a.e_part[g] = sm.n.err;
+  if (!last_block_done(&a.counters[0], gridDim.x)) return;
+
+  // ---- tail (the last group)
+  if (kFused) {
+    // the node phase's outputs for the restricted top-k, loaded before the
+    // demand rows so that both latencies overlap; stored after select_set
+    constexpr int R = kFusedMaxN * kMaxK / 256;
+    const int NK = N * a.k;
+    int pe[R];
+    float pl[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int x = t + 256 * r;
+      if (x < NK) {
+        pe[r] = a.nat_idx[x];
+        pl[r] = a.nat_logit[x];
+      }
+    }
+    float pm = 0.f;
+    double pz = 1.0;
+    if (t < N) {
+      pm = a.node_m[t];
+      pz = a.node_z[t];
+    }
+    constexpr int RL = kLgCap / 256;
+    const int NE = N * E;
+    const bool lg_lds = NE <= kLgCap;
+    float plg[RL];
+    if (lg_lds) {
+#pragma unroll
+      for (int r = 0; r < RL; ++r) plg[r] = a.logits[min(t + 256 * r, NE - 1)];
+    }
+    select_set(a, gridDim.x, sm.t.set);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int x = t + 256 * r;
+      if (x < NK) {
+        sm.t.top_e[x] = clamp_expert(pe[r], E);
+        sm.t.top_l[x] = pl[r];
+      }
+    }
+    if (t < N) {
+      sm.t.m[t] = pm;
+      sm.t.z[t] = pz;
+    }
+    if (lg_lds) {
+#pragma unroll
+      for (int r = 0; r < RL; ++r) {
+        const int x = t + 256 * r;
+        if (x < NE) sm.t.lg[x] = plg[r];
+      }
+    }
+    __syncthreads();
+    restricted_tail(a, sm.t, lg_lds);
+  } else {
+    select_set(a, gridDim.x, sm.t.set);
+  }
+}
+
+// one wave per node, 4 nodes per work-group (N > kFusedMaxN)
+__global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
+  __shared__ PermuteSmem<256> perm;
   const int lane = lane_id();
-  const int i = blockIdx.x * 16 + static_cast<int>(threadIdx.x >> 6);
+  const int i = blockIdx.x * kNodesPerWG + static_cast<int>(threadIdx.x >> 6);
   if (i < a.N) {
     const int E = a.E, k = a.k;
     const float* row = a.logits + static_cast<size_t>(i) * E;
@@ -421,7 +761,7 @@ __global__ __launch_bounds__(1024) void restricted_kernel(SelectArgs a) {
     double p = 0.0;
     if (lane < k) p = exp(static_cast<double>(row[my_sel]) - m) / z;
     double s = 0.0;
-    for (int j = 0; j < k; ++j) s += __shfl(p, j, kWave);
+    for (int j = 0; j < k; ++j) s += readlane_f64(p, j);  // slot order
     if (lane < k) {
       const double g = (a.flags & kFlagNoRenorm) ? p : p / s;
       a.topk_idx[static_cast<size_t>(i) * k + lane] = my_sel;
@@ -430,39 +770,48 @@ __global__ __launch_bounds__(1024) void restricted_kernel(SelectArgs a) {
   }
   if (a.counts) {
     if (last_block_done(&a.counters[1], gridDim.x))
-      permute_block(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
-                    a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats));
+      permute_block<256>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
+                         a.inv_pos, a.active, a.n_active, a.resident,
+                         static_cast<StatsDev*>(a.stats), perm);
   }
 }
 
 }  // namespace
 
 void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) {
-  const int tiles = ((E + kRT - 1) / kRT) * ((N + kRT - 1) / kRT);
-  int ks = 512 / tiles;
-  if (ks < 1) ks = 1;
+  // about 128 work-groups (groups x K slices), at most kMaxKSplit slices of
+  // at most kMaxSlice elements each, multiples of 64
+  const int groups = (N + kNodesPerWG - 1) / kNodesPerWG;
+  int ks = (128 + groups - 1) / groups;
+  if (ks > kMaxKSplit) ks = kMaxKSplit;
+  const int min_ks = (H + kMaxSlice - 1) / kMaxSlice;
+  if (ks < min_ks) ks = min_ks;
   if (ks > H / 64) ks = H / 64;
   int sl = (H + ks - 1) / ks;
   sl = (sl + 63) / 64 * 64;
   *kslice = sl;
   *ksplit = (H + sl - 1) / sl;
+  (void)E;
 }
 
+int node_workgroups(int N) { return (N + kNodesPerWG - 1) / kNodesPerWG; }
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  // with given logits the router only resets the arrival counter
   const bool lin = (a.flags & kFlagLogitsIn) != 0;
-  const dim3 grid = lin ? dim3(1, 1, 1) : dim3((a.E + kRT - 1) / kRT, (a.N + kRT - 1) / kRT, a.ksplit);
-  if (a.act_bf16)
-    router_partial_kernel<uint16_t><<<grid, 256, 0, stream>>>(
-        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w_router), a.N, a.E,
-        a.H, a.kslice, a.part, a.counters, !lin);
-  else
-    router_partial_kernel<float><<<grid, 256, 0, stream>>>(
-        static_cast<const float*>(a.x), static_cast<const float*>(a.w_router), a.N, a.E, a.H,
-        a.kslice, a.part, a.counters, !lin);
-  const int nb = (a.N + 15) / 16;
-  node_kernel<<<nb, 1024, 0, stream>>>(a);
-  restricted_kernel<<<nb, 1024, 0, stream>>>(a);
+  const dim3 grid(node_workgroups(a.N), lin ? 1 : a.ksplit, 1);
+  const bool fused = a.N <= kFusedMaxN;
+  if (a.act_bf16) {
+    if (fused)
+      front_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(a);
+    else
+      front_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (fused)
+      front_kernel<float, true><<<grid, 256, 0, stream>>>(a);
+    else
+      front_kernel<float, false><<<grid, 256, 0, stream>>>(a);
+  }
+  if (!fused) restricted_kernel<<<node_workgroups(a.N), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

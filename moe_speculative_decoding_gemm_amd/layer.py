@@ -44,7 +44,7 @@ class VerifyLayer:
         if nbytes == 0:
             raise L.AcceptMoEError(L.EINVAL, "acceptmoe_workspace_size",
                                    L.raw().acceptmoe_last_error().decode())
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.out = {"y": torch.empty((N, H), dtype=adt, device=dev)}
         if debug_outputs:
             self.out.update(

@@ -53,6 +53,8 @@ SMALL = [
     # fp8 weights with block scales and the shared expert; chains of 8
     ("dsv31", dict(E=20, k=3, H=384, I=256, N=40, n_chains=5, chain_len=8)),
     ("dsv31", dict(E=48, k=8, H=256, I=512, N=96, n_chains=12, chain_len=8)),
+    # more than 256 nodes: the restricted top-k runs as a kernel of its own
+    ("qwen3_30b", dict(E=40, k=6, H=192, I=128, N=300)),
 ]
 
 
@@ -132,7 +134,7 @@ def test_separate_entry_points_match_verify_block(lib):
     e_ = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
     elig, ti, tg = e_(E, dt=torch.uint8), e_(N, k), e_(N, k, dt=torch.float32)
     stats = lib.new_stats(dev)
-    ws = torch.empty(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
     lib.acceptmoe_select(sh, d["x"], d["w_router"], d["b_router"], None, d["parent"],
                          d["depth"], d["commit"], None, None, elig, ti, tg, stats, ws)
     counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)

@@ -31,7 +31,7 @@ def run_select(lib, cfg, b, flags=None, logits_in=None, resident="block"):
                topk_idx=torch.empty((N, k), dtype=torch.int32, device=dev),
                topk_gate=torch.empty((N, k), dtype=torch.float32, device=dev),
                stats=lib.new_stats(dev))
-    ws = torch.empty(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
     res = d["resident"] if isinstance(resident, str) else resident
     lin = None if logits_in is None else torch.from_numpy(logits_in).to(dev)
     lib.acceptmoe_select(sh, d["x"], d["w_router"], d["b_router"], lin, d["parent"],
