@@ -52,11 +52,28 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--flags", type=int, default=None, help="override shape flags (1 = natural)")
     ap.add_argument("--fixed-budget", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (for scaling HBM "
+                         "byte counters: FETCH_SIZE / WRITE_SIZE of a known-size copy)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the one-GPU hot path only: this build has no multi-GPU "
@@ -260,15 +277,38 @@ def main():
                       "r_eff_mean": round(statistics.mean(st["r_eff"] for st in stats), 3),
                       "expert_bytes": ebytes},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
-        "roofline": {"kernel": "gateup_kernel (gate/up projections + SwiGLU)",
+        "roofline": {"kernel": "expert_lds_kernel<gate/up> (gate/up projections + SwiGLU)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(cfg.name),
                      "avg_launch_us": round(statistics.mean(g_us), 3),
                      "algorithmic_bytes_per_launch": round(statistics.mean(gate_bytes))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE passes scaled by a known-size copy), or
+    None when there is none for this workload or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic {"):
+            rec = json.loads(line[len("traffic "):])
+    if rec is None:
+        return None
+    src = os.path.join(ROOT, "moe_speculative_decoding_gemm_amd", "csrc", "grouped.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("grouped_hip_sha256"):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(cfg, blocks, host_w, slots, seconds):

@@ -11,14 +11,15 @@
 //
 // One kernel (front_kernel, wave64, 256 threads per work-group) over a grid of
 // (node groups of 4) x (K slices of the router product):
-//   router   each work-group: the 4 nodes' logits over its K slice for all
-//            experts, fp32 FMAs with x in LDS (vector ALU: the router is a few
-//            MFLOP per block; the matrix cores are kept for the experts).
+//   router   each work-group: the 4 nodes' partial logits over its K slice for
+//            all experts on MFMA (16x16x32 bf16; fp32 inputs as eight
+//            16x16x4 steps), rows 0..3 of each 16x16 tile being the nodes.
 //   node     the last K-slice work-group of a group to finish: one wave per
 //            node sums the slice partials (+ bias), takes fp64 softmax
-//            statistics and the natural top-k by 64-bit (logit, ~index) keys,
-//            and adds the demand terms c[depth] * p of the node's top-k into
-//            one partial row per group.
+//            statistics and the natural top-k (k rounds of a wave max over
+//            32-bit order keys, ties to the lower index), and adds the demand
+//            terms c[depth] * p of the node's top-k into one partial row per
+//            group.
 //   tail     the last group to finish: demand per expert (fixed summation
 //            order), entropy, set size, anchor + fill and pruning by rank
 //            counting; then (N <= kFusedMaxN) every node's restricted top-k,

@@ -120,13 +120,15 @@ def test_layer_parity_full_sampled(lib, name, tokens):
     assert err <= TOL[cfg.w]
 
 
-def test_separate_entry_points_match_verify_block(lib):
+@pytest.mark.parametrize("pack", [False, True], ids=["rowmajor", "packed"])
+def test_separate_entry_points_match_verify_block(lib, pack):
     """acceptmoe_select -> moe_route_permute -> moe_grouped_swiglu (+ shared)
-    -> moe_combine reproduces verify_block bit for bit."""
+    -> moe_combine reproduces verify_block bit for bit, for either weight
+    layout (the grouped call gets the layout verify_block used)."""
     cfg = W.CONFIGS["dsv31"].with_(E=24, k=4, H=256, I=384, N=32, n_chains=4, chain_len=8)
     w = make_weights(cfg, device="cuda", gen_device="cpu")
     b = W.make_block(cfg, 2)
-    out, st = run_layer(lib, cfg, b, w)
+    out, st = run_layer(lib, cfg, b, w, pack=pack)
     d = upload_block(b)
     dev = "cuda"
     sh = shape_of(lib, cfg)
@@ -139,21 +141,27 @@ def test_separate_entry_points_match_verify_block(lib):
                          d["depth"], d["commit"], None, None, elig, ti, tg, stats, ws)
     counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)
     lib.moe_route_permute(N, k, E, ti, counts, offsets, sa, ip, act, na)
+    layout = lib.LAYOUT_PACKED if pack else lib.LAYOUT_ROWMAJOR
+    w13, w2, w13s, w2s = w["w13"], w["w2"], w["w13_shared"][None], w["w2_shared"][None]
+    if pack:
+        psh = shape_of(lib, cfg, w_layout=lib.LAYOUT_PACKED)
+        w13, w2 = lib.pack_experts(psh, w13, w2, E)
+        w13s, w2s = lib.pack_experts(psh, w13s, w2s, 1)
     y_perm = e_(N * k, H, dt=torch.float32)
     gws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, k, I, 2), dtype=torch.uint8,
                       device=dev)
-    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 2, d["x"], w["w13"], w["w2"], w["s13"], w["s2"],
-                           offsets, sa, act, na, y_perm, gws)
+    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 2, d["x"], w13, w2, w["s13"], w["s2"],
+                           offsets, sa, act, na, y_perm, gws, w_layout=layout)
     # shared expert = one-expert grouped call
     so = torch.tensor([0, N], dtype=torch.int32, device=dev)
     ss = torch.arange(N, dtype=torch.int32, device=dev)
     y_sh = e_(N, H, dt=torch.float32)
     sws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, 1, I, 2), dtype=torch.uint8,
                       device=dev)
-    lib.moe_grouped_swiglu(N, 1, 1, H, I, 1, 2, d["x"], w["w13_shared"][None],
-                           w["w2_shared"][None], w["s13_shared"][None], w["s2_shared"][None],
-                           so, ss, torch.zeros(1, dtype=torch.int32, device=dev),
-                           torch.ones(1, dtype=torch.int32, device=dev), y_sh, sws)
+    lib.moe_grouped_swiglu(N, 1, 1, H, I, 1, 2, d["x"], w13s, w2s, w["s13_shared"][None],
+                           w["s2_shared"][None], so, ss, torch.zeros(1, dtype=torch.int32, device=dev),
+                           torch.ones(1, dtype=torch.int32, device=dev), y_sh, sws,
+                           w_layout=layout)
     y = e_(N, H, dt=torch.bfloat16)
     lib.moe_combine(N, k, H, 1, y_perm, ip, tg, y_sh, y)
     torch.cuda.synchronize()
