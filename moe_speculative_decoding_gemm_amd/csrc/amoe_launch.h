@@ -35,10 +35,10 @@ struct SelectArgs {
   double* node_z;      // [N] softmax denominator
   int32_t* nat_idx;    // [N][k] natural top-k experts, slot order
   float* nat_logit;    // [N][k] their logits
-  double* d_part;      // [N/4][E] demand summed over each node work-group's 4 nodes
-  uint8_t* f_part;     // [N/4][E] bit 0: a root routes to the expert, bit 1: some node does
-  int32_t* e_part;     // [N/4] error bits of each node work-group
-  int32_t* counters;   // [2]: group arrivals (front kernel), restricted-kernel arrivals
+  double* d_part;      // [E][groups, padded] demand summed over each 4-node group
+  uint8_t* f_part;     // [E][groups, padded] bit 0: a root routes to the expert, bit 1: some node does
+  int32_t* e_part;     // [groups] error bits of each node group
+  int32_t* counters;   // [2]: [1] restricted-kernel arrivals ([0] unused)
   int32_t* gcount;     // [N/4]: K-slice arrivals per node group (zero between calls)
   // when non-null, the restricted top-k is followed by the grouping of the
   // assignments by expert (moe_route_permute's outputs)
@@ -54,7 +54,9 @@ struct SelectArgs {
 // selection, restricted top-k, gates (and the grouping when counts is set)
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 void select_plan(int N, int H, int E, int num_cu, int* ksplit, int* kslice);
-int node_workgroups(int N);  // node groups of the front kernel (rows of d_part)
+int node_workgroups(int N);  // node groups of the front kernel
+size_t dpart_elems(int N, int E);  // doubles of d_part (expert-major rows of group partials)
+size_t fpart_bytes(int N, int E);  // bytes of f_part (same rows)
 
 // grouping of the N*k assignments by expert; resident/stats may be null
 hipError_t launch_permute(int N, int k, int E, const int32_t* topk_idx, int32_t* counts,

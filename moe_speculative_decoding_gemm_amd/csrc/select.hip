@@ -9,8 +9,8 @@
 // residency-aware pruning; [AcceptMoE abstract] for restricting top-k to the
 // eligible set.
 //
-// One kernel (front_kernel, wave64, 256 threads per work-group) over a grid of
-// (node groups of 4) x (K slices of the router product):
+// front_kernel (wave64, 256 threads) over a grid of (node groups of 4) x
+// (K slices of the router product):
 //   router   each work-group: the 4 nodes' partial logits over its K slice for
 //            all experts on MFMA (16x16x32 bf16; fp32 inputs as eight
 //            16x16x4 steps), rows 0..3 of each 16x16 tile being the nodes.
@@ -19,15 +19,15 @@
 //            statistics and the natural top-k (k rounds of a wave max over
 //            32-bit order keys, ties to the lower index), and adds the demand
 //            terms c[depth] * p of the node's top-k into one partial row per
-//            group.
-//   tail     the last group to finish: demand per expert (fixed summation
-//            order), entropy, set size, anchor + fill and pruning by rank
-//            counting; then (N <= kFusedMaxN) every node's restricted top-k,
-//            the gates and the grouping by expert.  A node whose natural
-//            top-k lies inside the set keeps it (the k largest keys of all
-//            experts are the k largest of any superset of them); the others
-//            rank their set members' keys by counting.
-// For N > kFusedMaxN a second kernel (restricted_kernel, one wave per node)
+//            group (stored expert-major).
+// tail_kernel (one work-group of 1024 threads): demand per expert (group
+// partials summed in group order), entropy, set size, anchor + fill and
+// pruning by rank counting; then (N <= kFusedMaxN) every node's restricted
+// top-k, the gates and the grouping by expert.  A node whose natural top-k
+// lies inside the set keeps it (the k largest keys of all experts are the k
+// largest of any superset of them); the others rank their set members' keys
+// by counting.
+// For N > kFusedMaxN a third kernel (restricted_kernel, one wave per node)
 // takes the restricted top-k and gates, and its last work-group groups.
 // Every reduction has a fixed order: two runs give identical bits.  Arrival
 // counters are left at zero by the last arriver, so a zero-filled workspace
@@ -47,6 +47,13 @@ constexpr int kMaxSlice = 2048;  // K elements per router slice
 constexpr int kFusedMaxN = 256;  // largest N whose restricted top-k runs in the tail
 constexpr int kKeyCap = 4096;    // (node, member) keys per rank-counting pass
 constexpr int kLgCap = 8192;     // logits the tail holds in LDS (N * E up to this)
+constexpr int kTail = 1024;      // threads of the tail kernel (one work-group)
+
+// demand / flag partial rows are stored expert-major, one row of group
+// partials per expert, padded so that a row starts 16-byte aligned
+__host__ __device__ __forceinline__ int node_groups(int N) { return (N + kNodesPerWG - 1) / kNodesPerWG; }
+__host__ __device__ __forceinline__ int dpart_stride(int N) { return (node_groups(N) + 1) & ~1; }
+__host__ __device__ __forceinline__ int fpart_stride(int N) { return (node_groups(N) + 15) & ~15; }
 
 // MFMA operand fragment: 8 consecutive K elements of one row (x or W_r).
 // v_mfma_f32_16x16x32_bf16: A[m][kk] in lane m + 16g for kk in [8g, 8g+8),
@@ -100,6 +107,7 @@ struct SetSmem {
   double d[kMaxE];
   double key[kMaxE];
   int anchor[kMaxE], rank[kMaxE], elig[kMaxE];
+  int part[kTail];  // split_rank partial counts
   int err, na, nnat, nsel, ncand;
   double tot, h;
 };
@@ -118,12 +126,8 @@ struct TailSmem {
   union {
     uint64_t keys[kKeyCap];           // rank counting
     double p[kFusedMaxN * kMaxK];     // gate numerators
-    PermuteSmem<256> perm;
+    PermuteSmem<kTail> perm;
   } u;
-};
-union FrontSmem {
-  NodeSmem n;
-  TailSmem t;
 };
 
 // 32-bit order key of a logit: unsigned order = float order (-0 folded onto
@@ -271,26 +275,26 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
 // holds the demand of the experts that take part and a sentinel for the rest
 // (below or above every demand, so it never counts).  desc: order (key desc,
 // index asc); else (key asc, index desc).  The E x EP comparisons are split
-// over the 256 threads: thread (e, part) counts over one part of the keys and
-// the parts are added in LDS.  Call with the whole work-group; returns the
-// rank in threads t < E with take[t] set.
+// over the kTail threads: thread (e, part) counts over one part of the keys
+// and the parts are added in LDS.  Call with the whole work-group; returns
+// the rank in threads t < E with take[t] set.
 __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E, bool desc,
                                           const int* take) {
   const int t = threadIdx.x;
   const int EP = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
-  const int tpe = 256 / EP, e = t % EP, part = t / EP;
-  const int span = EP / tpe;  // a multiple of 16
+  const int tpe = kTail / EP, e = t % EP, part = t / EP;
+  const int span = EP / tpe;  // a multiple of 4
   int r = 0;
   if (e < E && take[e]) {
     const double de = key[e];
     const int f0 = part * span;
-    for (int f = f0; f < f0 + span; f += 8) {
-      // eight keys read first, then compared without branches
-      double df[8];
+    for (int f = f0; f < f0 + span; f += 4) {
+      // four keys read first, then compared without branches
+      double df[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) df[u] = key[f + u];
+      for (int u = 0; u < 4; ++u) df[u] = key[f + u];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const int strict = desc ? (df[u] > de) : (df[u] < de);
         const int tie = (df[u] == de) & (desc ? (f + u < e) : (f + u > e));
         r += strict | tie;
@@ -306,11 +310,12 @@ __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E
   return rank;
 }
 
-// One 256-thread work-group.  nwg partial rows of demand / flags / errors.
-// Leaves the eligible flags in sm.elig (and in a.eligible), statistics in
-// a.stats (n_active is filled by the grouping).
+// One kTail-thread work-group.  nwg partial rows (per expert, expert-major)
+// of demand / flags, nwg error words.  Leaves the eligible flags in sm.elig
+// (and in a.eligible), statistics in a.stats (n_active is filled by the
+// grouping).
 __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
-  static_assert(kMaxE == 256, "select_set runs one thread per expert slot");
+  static_assert(kMaxE == 256 && kTail >= kMaxE, "select_set keeps one thread per expert slot");
   const int t = threadIdx.x;
   const int E = a.E, k = a.k;
   const bool natural = (a.flags & kFlagNatural) != 0;
@@ -322,39 +327,42 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     sm.ncand = 0;
   }
   __syncthreads();
-  // demand per expert: partial rows summed in group order
+  // demand per expert: its row of group partials summed in group order
+  // (16-byte loads: two partials, sixteen flag bytes)
   int f = 0;
   double dsum = 0.0;
   if (t < E) {
-    constexpr int B = 16;
-    for (int w0 = 0; w0 < nwg; w0 += B) {
-      double dv[B];
-      int fv[B];
+    const int ds = dpart_stride(a.N), fs = fpart_stride(a.N);
+    const double* drow = a.d_part + static_cast<size_t>(t) * ds;
+    const uint8_t* frow = a.f_part + static_cast<size_t>(t) * fs;
+    constexpr int B = 8;  // 16-byte loads in flight per batch: 16 partials
+    for (int w0 = 0; w0 < nwg; w0 += 2 * B) {
+      f64x2_t dv[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (w0 + 2 * u < nwg) dv[u] = *reinterpret_cast<const f64x2_t*>(drow + w0 + 2 * u);
+      const u32x4_t fv = *reinterpret_cast<const u32x4_t*>(frow + w0);
 #pragma unroll
       for (int u = 0; u < B; ++u) {
-        if (w0 + u < nwg) {
-          dv[u] = a.d_part[static_cast<size_t>(w0 + u) * E + t];
-          fv[u] = a.f_part[static_cast<size_t>(w0 + u) * E + t];
-        }
+        if (w0 + 2 * u < nwg) dsum += dv[u][0];
+        if (w0 + 2 * u + 1 < nwg) dsum += dv[u][1];
       }
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        if (w0 + u < nwg) {
-          dsum += dv[u];
-          f |= fv[u];
-        }
-      }
+      for (int u = 0; u < 16; ++u)
+        if (w0 + u < nwg) f |= static_cast<int>((fv[u >> 2] >> (8 * (u & 3))) & 0xffu);
     }
     if (f & 1) atomicAdd(&sm.na, 1);
     if (f & 2) atomicAdd(&sm.nnat, 1);
   }
-  sm.d[t] = dsum;
-  sm.anchor[t] = f & 1;
-  for (int w = t; w < nwg; w += 256) {
+  if (t < kMaxE) {
+    sm.d[t] = dsum;
+    sm.anchor[t] = f & 1;
+  }
+  for (int w = t; w < nwg; w += kTail) {
     const int e = a.e_part[w];
     if (e) atomicOr(&sm.err, e);
   }
-  for (int dd = t; dd < a.n_depth; dd += 256) {
+  for (int dd = t; dd < a.n_depth; dd += kTail) {
     const float c = a.commit[dd];
     if (!(c >= 0.f) || isinf(c)) atomicOr(&sm.err, kErrCommit);
   }
@@ -381,8 +389,10 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
   }
   // fill order: (demand desc, index asc) over the non-anchor experts; anchors
   // and padding carry demand -1, below every real demand
-  sm.key[t] = (t < E && !sm.anchor[t]) ? sm.d[t] : -1.0;
-  sm.elig[t] = t < E && !sm.anchor[t];  // experts that take part in the fill
+  if (t < kMaxE) {
+    sm.key[t] = (t < E && !sm.anchor[t]) ? sm.d[t] : -1.0;
+    sm.elig[t] = t < E && !sm.anchor[t];  // experts that take part in the fill
+  }
   __syncthreads();
   const double tot = sm.tot;
   const double r_eff = tot > 0.0 ? exp(sm.h) : 0.0;
@@ -391,13 +401,13 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
   const int n_raw = a.fixed_budget > 0 ? a.fixed_budget : static_cast<int>(floor(r_eff + 0.5));
   const int n = min(E, max(max(n_raw, n_anchor), n_min));
   const int take = n - n_anchor;
-  const int fill_rank = split_rank(sm.key, sm.rank, E, true, sm.elig);
+  const int fill_rank = split_rank(sm.key, sm.part, E, true, sm.elig);
   int el = 0;
   if (t < E) {
     el = natural ? 1 : (sm.anchor[t] || fill_rank < take) ? 1 : 0;
     if (el) atomicAdd(&sm.nsel, 1);
   }
-  sm.elig[t] = el;
+  if (t < kMaxE) sm.elig[t] = el;
   __syncthreads();
   const int n_selfsize = sm.nsel;
   int n_remove = 0;
@@ -406,11 +416,13 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     if (cand) atomicAdd(&sm.ncand, 1);
     // pruning order among candidates: demand ascending, index descending;
     // non-candidates carry +infinity (never below a candidate's demand)
-    sm.key[t] = cand ? sm.d[t] : INFINITY;
-    sm.anchor[t] = cand;  // the anchor flags are no longer needed: candidates
+    if (t < kMaxE) {
+      sm.key[t] = cand ? sm.d[t] : INFINITY;
+      sm.anchor[t] = cand;  // the anchor flags are no longer needed: candidates
+    }
     __syncthreads();
     n_remove = max(0, min(a.reroute_budget, min(n_selfsize - n_min, sm.ncand)));
-    const int prune_rank = split_rank(sm.key, sm.rank, E, false, sm.anchor);
+    const int prune_rank = split_rank(sm.key, sm.part, E, false, sm.anchor);
     if (cand && prune_rank < n_remove) sm.elig[t] = 0;
     __syncthreads();
   }
@@ -431,7 +443,7 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
 }
 
 // ------------------------------------------------- restricted top-k tail ----
-// After select_set, by the same 256-thread work-group, for N <= kFusedMaxN,
+// After select_set, by the same kTail-thread work-group, for N <= kFusedMaxN,
 // with sm.top_e / top_l / m / z already holding the node phase's natural
 // top-k and softmax statistics: every node's top-k over the eligible set, the
 // gates, and (when a.counts is set) the grouping of the assignments by expert.
@@ -440,7 +452,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int N = a.N, E = a.E, k = a.k;
   const int NK = N * k;
-  for (int i = t; i < N; i += 256) sm.bad[i] = 0;
+  for (int i = t; i < N; i += kTail) sm.bad[i] = 0;
   if (wave == 0) {  // eligible experts in ascending order
     const int nm = wave_exclusive_scan_256(sm.set.elig, sm.set.rank, kMaxE);
     if (lane == 0) {
@@ -451,10 +463,10 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   __syncthreads();
   if (t < E && sm.set.elig[t]) sm.member[sm.set.rank[t]] = t;
   // nodes whose natural top-k leaves the set
-  for (int x = t; x < NK; x += 256)
+  for (int x = t; x < NK; x += kTail)
     if (!sm.set.elig[sm.top_e[x]]) sm.bad[x / k] = 1;
   __syncthreads();
-  for (int i = t; i < N; i += 256)
+  for (int i = t; i < N; i += kTail)
     if (sm.bad[i]) sm.needy[atomicAdd(&sm.nneedy, 1)] = i;
   __syncthreads();
   const int nm = sm.nmem, nneedy = sm.nneedy;
@@ -466,7 +478,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   for (int c0 = 0; c0 < nneedy; c0 += per) {
     const int cn = min(per, nneedy - c0);
     const int total = cn * nmp;
-    for (int x = t; x < total; x += 256) {
+    for (int x = t; x < total; x += kTail) {
       int r = static_cast<int>(static_cast<float>(x) * inv);
       if (r * nmp > x) --r;
       if ((r + 1) * nmp <= x) ++r;
@@ -480,7 +492,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
       sm.u.keys[x] = key;
     }
     __syncthreads();
-    for (int x = t; x < total; x += 256) {
+    for (int x = t; x < total; x += kTail) {
       int r = static_cast<int>(static_cast<float>(x) * inv);
       if (r * nmp > x) --r;
       if ((r + 1) * nmp <= x) ++r;
@@ -512,13 +524,13 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   }
   // gates: fp64 softmax scores of the chosen experts, renormalised over the
   // node's k slots in slot order
-  for (int x = t; x < NK; x += 256) {
+  for (int x = t; x < NK; x += kTail) {
     const int i = x / k;
     sm.u.p[x] = exp(static_cast<double>(sm.top_l[x]) - static_cast<double>(sm.m[i])) / sm.z[i];
   }
   __syncthreads();
   const bool renorm = (a.flags & kFlagNoRenorm) == 0;
-  for (int x = t; x < NK; x += 256) {
+  for (int x = t; x < NK; x += kTail) {
     const int i = x / k;
     double s = 0.0;
     for (int j = 0; j < k; ++j) s += sm.u.p[i * k + j];
@@ -528,7 +540,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   }
   __syncthreads();
   if (a.counts)
-    permute_block<256>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
+    permute_block<kTail>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
                        a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
                        sm.u.perm);
 }
@@ -611,12 +623,12 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
 }
 
 // ------------------------------------------------------------- kernel ----
-template <typename AT, bool kFused>
+template <typename AT>
 __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) FrontSmem sm;
+  __shared__ NodeSmem sm;
   const int t = threadIdx.x, wave = t >> 6, lane = lane_id();
   const int g = blockIdx.x, ks = blockIdx.y;
-  const int N = a.N, E = a.E, H = a.H;
+  const int N = a.N, E = a.E;
   const int n0 = g * kNodesPerWG;
   const int node = n0 + wave;  // this wave's node in the node phase
   const bool has_node = node < N;
@@ -653,79 +665,85 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
 
   // ---- node phase (the group's last K-slice work-group)
   for (int x = t; x < kMaxE; x += 256) {
-    sm.n.flags[x] = 0;
+    sm.flags[x] = 0;
 #pragma unroll
-    for (int w = 0; w < kNodesPerWG; ++w) sm.n.c[w][x] = 0.0;
+    for (int w = 0; w < kNodesPerWG; ++w) sm.c[w][x] = 0.0;
   }
-  if (t == 0) sm.n.err = 0;
+  if (t == 0) sm.err = 0;
   __syncthreads();
-  if (has_node) node_phase(a, node, wave, sm.n, d, p, dp, cf, bias);
+  if (has_node) node_phase(a, node, wave, sm, d, p, dp, cf, bias);
   __syncthreads();
+  const int ds = dpart_stride(N), fs = fpart_stride(N);
   for (int x = t; x < E; x += 256) {
     double dsum = 0.0;
 #pragma unroll
-    for (int w = 0; w < kNodesPerWG; ++w) dsum += sm.n.c[w][x];  // node order
-    a.d_part[static_cast<size_t>(g) * E + x] = dsum;
-    a.f_part[static_cast<size_t>(g) * E + x] = static_cast<uint8_t>(sm.n.flags[x]);
+    for (int w = 0; w < kNodesPerWG; ++w) dsum += sm.c[w][x];  // node order
+    a.d_part[static_cast<size_t>(x) * ds + g] = dsum;
+    a.f_part[static_cast<size_t>(x) * fs + g] = static_cast<uint8_t>(sm.flags[x]);
   }
-  if (t == 0) a.e_part[g] = sm.n.err;
-  if (!last_block_done(&a.counters[0], gridDim.x)) return;
+  if (t == 0) a.e_part[g] = sm.err;
+}
 
-  // ---- tail (the last group)
-  if (kFused) {
-    // the node phase's outputs for the restricted top-k, loaded before the
-    // demand rows so that both latencies overlap; stored after select_set
-    constexpr int R = kFusedMaxN * kMaxK / 256;
-    const int NK = N * a.k;
-    int pe[R];
-    float pl[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int x = t + 256 * r;
-      if (x < NK) {
-        pe[r] = a.nat_idx[x];
-        pl[r] = a.nat_logit[x];
-      }
-    }
-    float pm = 0.f;
-    double pz = 1.0;
-    if (t < N) {
-      pm = a.node_m[t];
-      pz = a.node_z[t];
-    }
-    constexpr int RL = kLgCap / 256;
-    const int NE = N * E;
-    const bool lg_lds = NE <= kLgCap;
-    float plg[RL];
-    if (lg_lds) {
-#pragma unroll
-      for (int r = 0; r < RL; ++r) plg[r] = a.logits[min(t + 256 * r, NE - 1)];
-    }
-    select_set(a, gridDim.x, sm.t.set);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int x = t + 256 * r;
-      if (x < NK) {
-        sm.t.top_e[x] = clamp_expert(pe[r], E);
-        sm.t.top_l[x] = pl[r];
-      }
-    }
-    if (t < N) {
-      sm.t.m[t] = pm;
-      sm.t.z[t] = pz;
-    }
-    if (lg_lds) {
-#pragma unroll
-      for (int r = 0; r < RL; ++r) {
-        const int x = t + 256 * r;
-        if (x < NE) sm.t.lg[x] = plg[r];
-      }
-    }
-    __syncthreads();
-    restricted_tail(a, sm.t, lg_lds);
-  } else {
-    select_set(a, gridDim.x, sm.t.set);
+// The set selection and, for N <= kFusedMaxN, every node's restricted top-k,
+// the gates and the grouping: one work-group of kTail threads, after the
+// front kernel.  The node phase's outputs are loaded first, all together.
+__global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
+  __shared__ __attribute__((aligned(16))) TailSmem sm;
+  const int t = threadIdx.x;
+  const int N = a.N, E = a.E;
+  const int nwg = node_groups(N);
+  const bool fused = N <= kFusedMaxN;
+  if (!fused) {
+    select_set(a, nwg, sm.set);
+    return;
   }
+  // natural top-k, its logits, max / sum of exp per node, and (when they
+  // fit) all logits, in 16-byte loads issued before the demand rows
+  const int NK = N * a.k;
+  const int NE = N * E;
+  const bool lg_lds = NE <= kLgCap;
+  constexpr int RL = kLgCap / kTail;  // 8 logits per thread
+  const int x4 = 4 * t;               // 4 top-k slots per thread (NK <= 4096)
+  u32x4_t pe, pl;
+  f32x4_t plg[RL / 4];
+  if (x4 < NK) {
+    pe = *reinterpret_cast<const u32x4_t*>(a.nat_idx + x4);
+    pl = *reinterpret_cast<const u32x4_t*>(a.nat_logit + x4);
+  }
+  if (lg_lds) {
+#pragma unroll
+    for (int r = 0; r < RL / 4; ++r) {
+      const int x = (t * (RL / 4) + r) * 4;
+      if (x < NE) plg[r] = *reinterpret_cast<const f32x4_t*>(a.logits + x);
+    }
+  }
+  float pm = 0.f;
+  double pz = 1.0;
+  if (t < N) {
+    pm = a.node_m[t];
+    pz = a.node_z[t];
+  }
+  select_set(a, nwg, sm.set);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (x4 + j < NK) {
+      sm.top_e[x4 + j] = clamp_expert(static_cast<int>(pe[j]), E);
+      sm.top_l[x4 + j] = __uint_as_float(pl[j]);
+    }
+  }
+  if (t < N) {
+    sm.m[t] = pm;
+    sm.z[t] = pz;
+  }
+  if (lg_lds) {
+#pragma unroll
+    for (int r = 0; r < RL / 4; ++r) {
+      const int x = (t * (RL / 4) + r) * 4;
+      if (x < NE) *reinterpret_cast<f32x4_t*>(&sm.lg[x]) = plg[r];
+    }
+  }
+  __syncthreads();
+  restricted_tail(a, sm, lg_lds);
 }
 
 // one wave per node, 4 nodes per work-group (N > kFusedMaxN)
@@ -795,24 +813,19 @@ void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) 
   (void)E;
 }
 
-int node_workgroups(int N) { return (N + kNodesPerWG - 1) / kNodesPerWG; }
+int node_workgroups(int N) { return node_groups(N); }
+size_t dpart_elems(int N, int E) { return static_cast<size_t>(dpart_stride(N)) * E; }
+size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N)) * E; }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const bool lin = (a.flags & kFlagLogitsIn) != 0;
-  const dim3 grid(node_workgroups(a.N), lin ? 1 : a.ksplit, 1);
-  const bool fused = a.N <= kFusedMaxN;
-  if (a.act_bf16) {
-    if (fused)
-      front_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(a);
-    else
-      front_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(a);
-  } else {
-    if (fused)
-      front_kernel<float, true><<<grid, 256, 0, stream>>>(a);
-    else
-      front_kernel<float, false><<<grid, 256, 0, stream>>>(a);
-  }
-  if (!fused) restricted_kernel<<<node_workgroups(a.N), 256, 0, stream>>>(a);
+  const dim3 grid(node_groups(a.N), lin ? 1 : a.ksplit, 1);
+  if (a.act_bf16)
+    front_kernel<uint16_t><<<grid, 256, 0, stream>>>(a);
+  else
+    front_kernel<float><<<grid, 256, 0, stream>>>(a);
+  tail_kernel<<<1, kTail, 0, stream>>>(a);
+  if (a.N > kFusedMaxN) restricted_kernel<<<node_groups(a.N), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
