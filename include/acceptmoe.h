@@ -133,12 +133,12 @@ typedef struct acceptmoe_stats {
  *   topk_idx  [N,k] int32            topk_gate [N,k] fp32
  *   stats     one acceptmoe_stats (device)
  *   ws        workspace of at least acceptmoe_select_workspace_size(shape) bytes,
- *             device memory owned by the caller.  Its first 4 KiB hold the
- *             kernels' arrival counters: zero-fill the workspace once before
- *             its first use (hipMemset at allocation); every call leaves the
- *             counters at zero again, so it needs no clearing between calls,
- *             also when the shape changes.  Calls that share a workspace
- *             must not overlap in time (same stream, or synchronised).
+ *             device memory owned by the caller.  It holds the kernels'
+ *             arrival counters: zero-fill the workspace once before its first
+ *             use (hipMemset at allocation); every call leaves the counters
+ *             at zero again, so it needs no clearing between calls, also when
+ *             the shape changes.  Calls that share a workspace must not
+ *             overlap in time (same stream, or synchronised).
  * ------------------------------------------------------------------------- */
 size_t acceptmoe_select_workspace_size(const acceptmoe_shape* shape);
 int acceptmoe_select(const acceptmoe_shape* shape, const void* x, const void* w_router,

@@ -148,32 +148,4 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   }
 }
 
-// Last-arriver election: every thread of the work-group calls this after its
-// global writes.  Returns true in exactly one work-group of the grid -- the
-// last to arrive -- after which that work-group sees every other
-// work-group's writes.  The barrier completes the writes of all waves at
-// work-group scope; one thread then makes them visible at device scope
-// (release) before it counts the arrival, and the last arriver's thread
-// acquires before the second barrier.  One device-scope fence per
-// work-group, not one per wave: each such fence writes back the L2 of its
-// XCD, and many of them in flight serialise.  The counter must be zero at
-// kernel start; the last work-group resets it, so it stays zero between
-// launches.
-__device__ __forceinline__ bool last_block_done(int* counter, int nblocks) {
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const int prev = atomicAdd(counter, 1);
-    const bool last = prev == nblocks - 1;
-    if (last) {
-      __threadfence();
-      *counter = 0;  // ready for the next launch
-    }
-    s_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  return s_last != 0;
-}
-
 }  // namespace amoe

@@ -55,6 +55,11 @@ SMALL = [
     ("dsv31", dict(E=48, k=8, H=256, I=512, N=96, n_chains=12, chain_len=8)),
     # more than 256 nodes: the restricted top-k runs as a kernel of its own
     ("qwen3_30b", dict(E=40, k=6, H=192, I=128, N=300)),
+    # more work items than two per CU: the expert kernels cut items between
+    # work-groups (gate/up, then down; fp8 with NT = 2 and the shared expert)
+    ("qwen3_30b", dict(E=40, k=8, H=192, I=2112, N=64)),
+    ("qwen3_30b", dict(E=40, k=8, H=2112, I=192, N=64)),
+    ("dsv31", dict(E=24, k=8, H=256, I=2304, N=64, n_chains=8, chain_len=8)),
 ]
 
 
@@ -148,7 +153,7 @@ def test_separate_entry_points_match_verify_block(lib, pack):
         w13, w2 = lib.pack_experts(psh, w13, w2, E)
         w13s, w2s = lib.pack_experts(psh, w13s, w2s, 1)
     y_perm = e_(N * k, H, dt=torch.float32)
-    gws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, k, I, 2), dtype=torch.uint8,
+    gws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, k, I, 2), dtype=torch.uint8,
                       device=dev)
     lib.moe_grouped_swiglu(N, k, E, H, I, 1, 2, d["x"], w13, w2, w["s13"], w["s2"],
                            offsets, sa, act, na, y_perm, gws, w_layout=layout)
@@ -156,7 +161,7 @@ def test_separate_entry_points_match_verify_block(lib, pack):
     so = torch.tensor([0, N], dtype=torch.int32, device=dev)
     ss = torch.arange(N, dtype=torch.int32, device=dev)
     y_sh = e_(N, H, dt=torch.float32)
-    sws = torch.empty(lib.moe_grouped_swiglu_workspace_size(N, 1, I, 2), dtype=torch.uint8,
+    sws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, 1, I, 2), dtype=torch.uint8,
                       device=dev)
     lib.moe_grouped_swiglu(N, 1, 1, H, I, 1, 2, d["x"], w13s, w2s, w["s13_shared"][None],
                            w["s2_shared"][None], so, ss, torch.zeros(1, dtype=torch.int32, device=dev),
@@ -169,8 +174,11 @@ def test_separate_entry_points_match_verify_block(lib, pack):
     assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
 
 
-def test_determinism(lib):
-    cfg = W.CONFIGS["qwen3_30b"].with_(E=64, H=512, I=256, N=64)
+@pytest.mark.parametrize("over", [dict(E=64, H=512, I=256, N=64),
+                                  dict(E=40, k=8, H=192, I=2112, N=64)],
+                         ids=["whole_items", "split_items"])
+def test_determinism(lib, over):
+    cfg = W.CONFIGS["qwen3_30b"].with_(**over)
     w = make_weights(cfg, device="cuda", gen_device="cpu")
     b = W.make_block(cfg, 4)
     o1, s1 = run_layer(lib, cfg, b, w)
@@ -178,6 +186,44 @@ def test_determinism(lib):
     for key in o1:
         assert torch.equal(o1[key].view(torch.uint8), o2[key].view(torch.uint8)), key
     assert s1 == s2
+
+
+@pytest.mark.parametrize("pack", [False, True], ids=["rowmajor", "packed"])
+def test_grouped_expert_with_more_rows_than_tokens(lib, pack):
+    """moe_grouped_swiglu with a grouping in which tokens repeat within an
+    expert (100 rows for 64 tokens), with enough work items that the kernels
+    cut items between work-groups: every row must match the oracle's grouped
+    SwiGLU, the rows past the first 64 included."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=8, k=8, H=256, I=2560, N=64)
+    N, k, E, H, I = cfg.N, cfg.k, cfg.E, cfg.H, cfg.I
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 5)
+    # the last expert's items are among those cut into pieces
+    te = np.array([60, 60, 60, 60, 60, 60, 52, 100])
+    assert te.sum() == N * k
+    offsets = np.concatenate([[0], np.cumsum(te)]).astype(np.int32)
+    sa = np.random.default_rng(7).permutation(N * k).astype(np.int32)
+    perm = dict(offsets=offsets, sorted_assign=sa, active=np.arange(E))
+    dev = "cuda"
+    t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    layout = lib.LAYOUT_PACKED if pack else lib.LAYOUT_ROWMAJOR
+    w13, w2 = w["w13"], w["w2"]
+    if pack:
+        w13, w2 = lib.pack_experts(shape_of(lib, cfg, w_layout=lib.LAYOUT_PACKED), w13, w2, E)
+    y_perm = torch.zeros(N * k, H, dtype=torch.float32, device=dev)
+    gws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, k, I, 1), dtype=torch.uint8,
+                      device=dev)
+    x = b.x.to(dev)
+    for _ in range(2):  # the second call reuses the workspace the first left
+        say(f"grouped repeated-token rows pack={pack}")
+        lib.moe_grouped_swiglu(N, k, E, H, I, 1, 1, x, w13, w2, None, None, t32(offsets),
+                               t32(sa), t32(np.arange(E)), t32([E]), y_perm, gws,
+                               w_layout=layout)
+        torch.cuda.synchronize()
+        ref = O.grouped_swiglu(W.to_exact_f64(b.x), expert_fn_from(cfg, w), perm, k)
+        err = max_rel_err(y_perm, ref)
+        say(f"  rel err {err:.2e}")
+        assert err <= TOL["bf16"], err
 
 
 def test_natural_mode_layer(lib):
