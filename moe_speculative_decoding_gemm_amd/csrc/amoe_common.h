@@ -169,6 +169,40 @@ __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) 
 // work-group barrier alone does not wait for them.
 __device__ __forceinline__ void wait_global_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Device-scope (agent) stores and loads: they bypass the caches that are
+// not coherent across XCDs (the per-XCD L2 and the CU's L1), so data that
+// work-groups of one kernel hand to each other through them needs no cache
+// write-back or invalidation -- whole-cache operations that stall the other
+// waves of the XCD.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Last-arriver election for data written with store_dev and read with
+// load_dev.  Every thread of the work-group calls it after its store_dev
+// writes; it returns true in exactly one of the nblocks work-groups counting
+// on the same counter, the last to arrive, which may then load_dev what the
+// others wrote.  Each wave waits until its device-scope stores are complete
+// before the barrier; one thread then counts the arrival with an atomic
+// whose returned value decides.  The counter must be zero before the first
+// arrival; the last arriver resets it.
+__device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks) {
+  __shared__ int s_last_dev;
+  wait_global_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == nblocks - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last_dev = last ? 1 : 0;
+  }
+  __syncthreads();
+  return s_last_dev != 0;
+}
+
 // Last-arriver election: every thread of the work-group calls this after its
 // global writes.  Returns true in exactly one work-group of the nblocks that
 // count on the same counter -- the last to arrive -- after which that

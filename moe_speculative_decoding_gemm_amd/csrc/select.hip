@@ -14,6 +14,9 @@
 //   router   each work-group: the 4 nodes' partial logits over its K slice for
 //            all experts on MFMA (16x16x32 bf16; fp32 inputs as eight
 //            16x16x4 steps), rows 0..3 of each 16x16 tile being the nodes.
+//            The partials are stored and read back at device scope, so the
+//            hand-over to the group's last work-group needs no cache
+//            write-back or invalidation (whole-L2 operations).
 //   node     the last K-slice work-group of a group to finish: one wave per
 //            node sums the slice partials (+ bias), takes fp64 softmax
 //            statistics and the natural top-k (k rounds of a wave max over
@@ -178,7 +181,7 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
       const float* pp = a.part + static_cast<size_t>(i) * E + e;
 #pragma unroll
       for (int s = 0; s < kMaxKSplit; ++s)
-        if (valid[q] && s < a.ksplit) pv[q][s] = pp[s * stride];
+        if (valid[q] && s < a.ksplit) pv[q][s] = load_dev(pp + s * stride);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -616,7 +619,7 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
       if (e < E) {
 #pragma unroll
         for (int r = 0; r < kNodesPerWG; ++r)
-          if (n0 + r < N) a.part[(static_cast<size_t>(ks) * N + n0 + r) * E + e] = acc[tt][r];
+          if (n0 + r < N) store_dev(a.part + (static_cast<size_t>(ks) * N + n0 + r) * E + e, acc[tt][r]);
       }
     }
   }
@@ -658,7 +661,8 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
       router_partials<AT, 3>(a, g, ks, wave, lane, node, d, p, cf, dp);
     else
       router_partials<AT, 4>(a, g, ks, wave, lane, node, d, p, cf, dp);
-    if (!last_block_done(&a.gcount[g], gridDim.y)) return;
+    // partials travel at device scope: no cache write-back or invalidation
+    if (!last_arrival_dev(&a.gcount[g], gridDim.y)) return;
   } else {
     node_deps(a, node, d, p, cf, dp);
   }
