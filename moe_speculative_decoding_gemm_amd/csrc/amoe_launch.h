@@ -82,6 +82,10 @@ struct GroupedArgs {
   void* h_perm;  // [N*k][I] bf16 (fp32 when w_kind == 0)
   int num_cu;
   int packed;    // w13 / w2 are in the packed layout (pack_experts)
+  // bf16 / fp8 down projection: write the output of routed row t to row
+  // sorted_assign[t] of y_perm (token-major assignment order, i*k + j)
+  // instead of row t
+  int tok_rows;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);
@@ -92,6 +96,7 @@ size_t packed_bytes(int which, int w_kind, int E, int H, int I);
 hipError_t launch_pack(int which, int w_kind, int E, int H, int I, const void* src, void* dst,
                        hipStream_t stream);
 
+// inv_pos == nullptr: y_perm rows are in token-major assignment order
 hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm,
                           const int32_t* inv_pos, const float* topk_gate, const float* y_shared,
                           void* y, hipStream_t stream);

@@ -371,6 +371,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.h_perm = ws;
   a.num_cu = num_cu();
   a.packed = w_layout == ACCEPTMOE_LAYOUT_PACKED;
+  a.tok_rows = 0;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -501,6 +502,9 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.h_perm = w.h_perm;
   g.num_cu = num_cu();
   g.packed = s->w_layout == ACCEPTMOE_LAYOUT_PACKED;
+  // bf16 / fp8 weights: the down projection writes token-major rows, so the
+  // combine gathers without inv_pos (same values, same arithmetic)
+  g.tok_rows = g.w_kind != 0;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
   rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
@@ -530,11 +534,12 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.n_active = w.sh_n_active;
     gs.y_perm = w.sh_y;
     gs.h_perm = w.sh_h;
+    gs.tok_rows = 0;
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
     if (rc) return rc;
   }
   rc = hip_status(amoe::launch_combine(s->N, s->k, s->H, s->act_dtype == ACCEPTMOE_BF16,
-                                       w.y_perm, w.inv_pos, topk_gate,
+                                       w.y_perm, g.tok_rows ? nullptr : w.inv_pos, topk_gate,
                                        shared ? w.sh_y : nullptr, out->y, stream),
                   "verify_block/combine");
   timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);

@@ -418,6 +418,7 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
   using WTp = typename WeightT<WK>::T;
   using BR = typename BRaw<WK>::T;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * LDK];
+  __shared__ int s_row[ROWS];  // down, tok_rows: output row of each routed row
 
   const int H = a.H, I = a.I, k = a.k;
   const int K = GATEUP ? H : I;
@@ -571,6 +572,11 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
       load_b(bq[0], 0);
       stage_load(sv[1], min(1, nchunks - 1));
       load_b(bq[1], min(1, nchunks - 1));
+      // down, token-major output: each routed row's assignment index, loaded
+      // behind the pipeline's loads and used only by the epilogue
+      const bool tok = !GATEUP && a.tok_rows;
+      int my_row = 0;
+      if (tok) my_row = a.sorted_assign[off + min(mg + lane, te - 1)];
       stage_store(sv[0], 0);
       __syncthreads();
       auto body_main = [&](auto ic, int c) {
@@ -606,6 +612,10 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
           body_tail(I1{}, c + q);
       }
 
+      if (tok) {
+        if (t < ROWS) s_row[t] = my_row;
+        __syncthreads();
+      }
       // epilogue: lane (r, g) holds D[m = 4g + j][n = r] of each tile
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -622,7 +632,8 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
                 static_cast<uint16_t*>(a.h_perm)[static_cast<size_t>(off + m) * I + orow[nt]] =
                     f32_to_bf16(silu(v) * up);
             } else if (m < te) {
-              a.y_perm[static_cast<size_t>(off + m) * H + orow[nt]] = v;
+              const int row = tok ? s_row[m - mg] : off + m;
+              a.y_perm[static_cast<size_t>(row) * H + orow[nt]] = v;
             }
           }
         }

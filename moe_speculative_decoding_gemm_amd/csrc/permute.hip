@@ -39,7 +39,9 @@ __global__ void shared_grouping_kernel(int N, int32_t* offsets, int32_t* sorted_
 
 // y[i, h..h+3] = sum_j g[i][j] * y_perm[inv_pos[i*k+j]][h..h+3] (+ y_shared),
 // summed in slot order j = 0..k-1; all loads of a thread are issued up front.
-template <bool kBf16>
+// kTok: the rows are already in token-major order (row i*k + j), so the
+// loads need no inv_pos round trip first; the arithmetic is the same.
+template <bool kBf16, bool kTok>
 __global__ __launch_bounds__(256) void combine_kernel(int N, int k, int H,
                                                       const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv_pos,
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int N, int k, int H,
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
-      row[j] = inv_pos[static_cast<size_t>(i) * k + j];
+      row[j] = kTok ? i * k + j : inv_pos[static_cast<size_t>(i) * k + j];
       g[j] = gate[static_cast<size_t>(i) * k + j];
     }
   }
@@ -103,12 +105,21 @@ hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm
                           void* y, hipStream_t stream) {
   const size_t n = static_cast<size_t>(N) * (H / 4);
   const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
-  if (act_bf16)
-    combine_kernel<true><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
-                                                     y_shared, y);
-  else
-    combine_kernel<false><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
-                                                      y_shared, y);
+  if (act_bf16) {
+    if (inv_pos)
+      combine_kernel<true, false><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
+                                                              y_shared, y);
+    else
+      combine_kernel<true, true><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
+                                                             y_shared, y);
+  } else {
+    if (inv_pos)
+      combine_kernel<false, false><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos,
+                                                               topk_gate, y_shared, y);
+    else
+      combine_kernel<false, true><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos,
+                                                              topk_gate, y_shared, y);
+  }
   return hipGetLastError();
 }
 
