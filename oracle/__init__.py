@@ -39,6 +39,9 @@ from .acceptmoe import (  # noqa: F401
     F_NATURAL,
     F_NO_RENORM,
     F_LOGITS_IN,
+    F_DEMAND_FULL,
+    F_NO_ANCHOR,
+    F_UNIT_COMMIT,
     OracleInputError,
     router_logits,
     softmax64,

@@ -34,6 +34,13 @@ Readings taken where the pages are silent (each also listed in the design doc):
   with no replacement.
 * gates are the softmax scores of the chosen k renormalised to sum to one
   (raw scores under ``F_NO_RENORM``).
+* selector variants ([AcceptMoE news §01, §04]): MoE-Spec keeps a fixed
+  number B of the highest-ranked experts per layer and weighs every draft
+  position the same when it aggregates router scores; here that is
+  ``F_UNIT_COMMIT | F_NO_ANCHOR`` with ``fixed_budget = B``, the scores
+  aggregated as in AcceptMoE (natural top-k of each node).  AcceptMoE-B is
+  AcceptMoE with ``fixed_budget = B``.  ``F_DEMAND_FULL`` takes the literal
+  alternative reading of the demand: every expert's softmax score counts.
 * the expert FFN is SwiGLU: silu(x Wg^T) * (x Wu^T), then times Wd^T, no biases.
 
 Parity status: every public function here is pinned by the CPU tests
@@ -54,6 +61,10 @@ import numpy as np
 F_NATURAL = 1 << 0    # every expert eligible: natural routing
 F_NO_RENORM = 1 << 1  # gates are the raw softmax scores of the chosen experts
 F_LOGITS_IN = 1 << 2  # logits are given, the router product is skipped
+# selector variants on the same steps (baselines the pages compare against)
+F_DEMAND_FULL = 1 << 3   # demand sums every expert's score, not only the natural top-k's
+F_NO_ANCHOR = 1 << 4     # no root anchor
+F_UNIT_COMMIT = 1 << 5   # every draft position weighs 1 (commitment table ignored)
 
 # error bits for inputs the method cannot process
 ERR_BAD_TREE = 1 << 0   # a node's parent is not an earlier node, or depths disagree
@@ -152,13 +163,15 @@ def validate_tree(parent, depth, n_depth: int) -> int:
 
 
 # ---------------------------------------------------------------- step 3 --
-def demand(p, nat, depth, commit) -> np.ndarray:
+def demand(p, nat, depth, commit, full: bool = False) -> np.ndarray:
     """Commitment-weighted demand D_e = sum_i c[depth_i] * p_ie * [e in nat_i].
 
     [AcceptMoE news §02; AcceptMoE abstract]: the router's scores are weighted
     by each node's commitment probability (the chance that the node ends up in
     the accepted prefix, estimated offline per draft position) and summed per
     expert.  Only the experts a node would itself route to count for it.
+    ``full``: the literal alternative reading, D_e = sum_i c[depth_i] * p_ie
+    over every expert.  Nodes are summed in index order.
     """
     p = np.asarray(p, dtype=np.float64)
     nat = np.asarray(nat)
@@ -166,8 +179,9 @@ def demand(p, nat, depth, commit) -> np.ndarray:
     D = np.zeros(e, dtype=np.float64)
     for i in range(n):
         w = float(commit[int(depth[i])])
-        for ex in nat[i]:
-            D[int(ex)] += w * p[i, int(ex)]
+        experts = range(e) if full else (int(ex) for ex in nat[i])
+        for ex in experts:
+            D[ex] += w * p[i, ex]
     return D
 
 
@@ -440,8 +454,9 @@ def select(*, k: int, parent, depth, commit, x=None, w_router=None,
     N, E = logits.shape
     p = softmax64(logits)
     nat = natural_topk(logits, k)
-    D = demand(p, nat, depth, commit)
-    anchor = root_anchor(nat, parent)
+    weights = np.ones(n_depth, dtype=np.float64) if flags & F_UNIT_COMMIT else commit
+    D = demand(p, nat, depth, weights, full=bool(flags & F_DEMAND_FULL))
+    anchor = set() if flags & F_NO_ANCHOR else root_anchor(nat, parent)
     r_eff = effective_rank(D)
     n, n_min = self_size(r_eff, len(anchor), E, k, min_set, fixed_budget)
     margins = {}
