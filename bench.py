@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--stage-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selector-variant comparison (natural routing, AcceptMoE-B, "
+                         "MoE-Spec, full-softmax demand on the same kernels and blocks)")
+    ap.add_argument("--variant-steps", type=int, default=200)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--flags", type=int, default=None, help="override shape flags (1 = natural)")
     ap.add_argument("--fixed-budget", type=int, default=None)
@@ -243,6 +247,14 @@ def main():
     achieved = sum(gate_bytes) / (sum(g_us) * 1e-6) / 1e9
     log("stages (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
 
+    # ------------------------------------------- selector variants (same kernels) --
+    variants = None
+    if not args.no_variants:
+        variants = selector_variants(M, torch, layers, dblocks, slots, S,
+                                     statistics.mean(U), args.variant_steps)
+        log("selector variants (us/block, U): " + ", ".join(
+            f"{k} {v['us_per_block']:.1f} {v['U_mean']:.1f}" for k, v in variants.items()))
+
     # ------------------------------------------------------- CPU baseline --
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,6 +297,7 @@ def main():
                      "avg_launch_us": round(statistics.mean(g_us), 3),
                      "algorithmic_bytes_per_launch": round(statistics.mean(gate_bytes))},
         "cpu_baseline": cpu,
+        "selector_variants": variants,
     }
     print(json.dumps(result), flush=True)
 
@@ -309,6 +322,71 @@ def measured_traffic(workload):
     if sha != rec.get("grouped_hip_sha256"):
         return None
     return rec["bytes_per_launch"]
+
+
+def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):
+    """Microseconds per block and active experts of selector variants on the
+    same kernels, weights and blocks: natural routing (every expert
+    eligible), AcceptMoE (self-sized), AcceptMoE-B and MoE-Spec at the same
+    fixed budgets (B = AcceptMoE's mean U, and 16), and the full-softmax
+    reading of the demand.  Each is graph-replayed like the headline run."""
+    B = max(1, int(round(u_mean)))
+    base = layers[0].shape
+    spec = M.F_UNIT_COMMIT | M.F_NO_ANCHOR
+    plan = [("natural", dict(flags=base.flags | M.F_NATURAL)),
+            ("acceptmoe", dict()),
+            (f"acceptmoe_b{B}", dict(fixed_budget=B)),
+            (f"moe_spec_b{B}", dict(flags=base.flags | spec, fixed_budget=B)),
+            ("acceptmoe_b16", dict(fixed_budget=16)),
+            ("moe_spec_b16", dict(flags=base.flags | spec, fixed_budget=16)),
+            ("full_softmax_demand", dict(flags=base.flags | M.F_DEMAND_FULL))]
+    res = {}
+    for name, fields in plan:
+        vl = [layer.variant(**fields) for layer in layers]
+
+        def run_v(s, vl=vl):
+            bi, li = slots[s]
+            d = dblocks[bi]
+            return vl[li].run(d["x"], d["parent"], d["depth"], d["commit"],
+                              resident=d["resident"])
+        st = []
+        for s in range(S):
+            out = run_v(s)
+            torch.cuda.synchronize()
+            st.append(M.decode_stats(out["stats"]))
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for s in range(S):
+                run_v(s)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs = []
+        for s in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_v(s)
+            graphs.append(g)
+        for i in range(S):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            graphs[i % S].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us_per_block": round(us, 3),
+                     "U_mean": statistics.mean(x["n_active"] for x in st),
+                     "eligible_mean": statistics.mean(x["n_eligible"] for x in st),
+                     "budget": fields.get("fixed_budget", 0)}
+        del graphs
+    nat = res["natural"]["us_per_block"]
+    for v in res.values():
+        v["speedup_vs_natural"] = round(nat / v["us_per_block"], 4)
+    return res
 
 
 def cpu_baseline(cfg, blocks, host_w, slots, seconds):

@@ -65,7 +65,16 @@ typedef enum {
 enum {
   ACCEPTMOE_F_NATURAL = 1u << 0,   /* every expert eligible: natural routing (standard SD) */
   ACCEPTMOE_F_NO_RENORM = 1u << 1, /* gates = raw softmax scores of the chosen experts     */
-  ACCEPTMOE_F_LOGITS_IN = 1u << 2  /* read logits_in instead of computing x W_r^T + b_r    */
+  ACCEPTMOE_F_LOGITS_IN = 1u << 2, /* read logits_in instead of computing x W_r^T + b_r    */
+  /* Selector variants on the same kernels ([AcceptMoE news §01, §04]).
+   * MoE-Spec keeps a fixed number B of the highest-ranked experts and weighs
+   * every draft position alike: F_UNIT_COMMIT | F_NO_ANCHOR with
+   * fixed_budget = B.  AcceptMoE-B: fixed_budget = B alone.               */
+  ACCEPTMOE_F_DEMAND_FULL = 1u << 3, /* demand sums every expert's score, not only each node's
+                                        natural top-k                                       */
+  ACCEPTMOE_F_NO_ANCHOR = 1u << 4,   /* no root anchor                                       */
+  ACCEPTMOE_F_UNIT_COMMIT = 1u << 5  /* every draft position weighs 1 (commit table ignored
+                                        for the demand; still validated)                    */
 };
 
 /* bits of acceptmoe_stats.err_flags */

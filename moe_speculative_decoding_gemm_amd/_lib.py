@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libacceptmo
 OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 F_NATURAL, F_NO_RENORM, F_LOGITS_IN = 1, 2, 4
+F_DEMAND_FULL, F_NO_ANCHOR, F_UNIT_COMMIT = 8, 16, 32
 LAYOUT_ROWMAJOR, LAYOUT_PACKED = 0, 1
 ERR_BAD_TREE, ERR_DEPTH, ERR_NONFINITE, ERR_COMMIT = 1, 2, 4, 8
 

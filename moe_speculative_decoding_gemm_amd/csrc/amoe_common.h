@@ -26,6 +26,10 @@ constexpr int kErrCommit = 8;
 constexpr uint32_t kFlagNatural = 1u;
 constexpr uint32_t kFlagNoRenorm = 2u;
 constexpr uint32_t kFlagLogitsIn = 4u;
+constexpr uint32_t kFlagDemandFull = 8u;   // demand over every expert's score
+constexpr uint32_t kFlagNoAnchor = 16u;    // no root anchor
+constexpr uint32_t kFlagUnitCommit = 32u;  // every draft position weighs 1
+constexpr uint32_t kFlagsKnown = 63u;
 
 // ---------------------------------------------------------------- bf16 ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -88,7 +88,7 @@ int check_shape(const acceptmoe_shape* s, bool need_i) {
   if (!dtype_pair_ok(s->act_dtype, s->w_dtype))
     return fail(ACCEPTMOE_ENOTSUP, "unsupported dtype pair (act %d, weights %d)", s->act_dtype,
                 s->w_dtype);
-  if (s->flags & ~7u) return fail(ACCEPTMOE_ENOTSUP, "unknown flag bits %#x", s->flags);
+  if (s->flags & ~63u) return fail(ACCEPTMOE_ENOTSUP, "unknown flag bits %#x", s->flags);
   if (s->w_layout != ACCEPTMOE_LAYOUT_ROWMAJOR && s->w_layout != ACCEPTMOE_LAYOUT_PACKED)
     return fail(ACCEPTMOE_ENOTSUP, "unknown weight layout %d", s->w_layout);
   if (s->w_layout == ACCEPTMOE_LAYOUT_PACKED && s->w_dtype == ACCEPTMOE_F32)

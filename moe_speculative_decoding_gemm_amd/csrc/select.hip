@@ -246,15 +246,21 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
     a.nat_idx[static_cast<size_t>(i) * k + lane] = my_e;
     a.nat_logit[static_cast<size_t>(i) * k + lane] = order_logit(my_o);
   }
-  const double c = static_cast<double>(cf);
-  const int fl = p == -1 ? 3 : 2;
+  // demand terms: the node's weight times its score of every natural top-k
+  // expert (of every expert under kFlagDemandFull); the weight is the
+  // commitment probability of its depth (1 under kFlagUnitCommit).  Flag bit
+  // 1: natural top-k (for the union statistic); bit 0: anchor (a root's
+  // natural top-k, unless kFlagNoAnchor).
+  const bool full = (a.flags & kFlagDemandFull) != 0;
+  const double c = (a.flags & kFlagUnitCommit) ? 1.0 : static_cast<double>(cf);
+  const int fl = (p == -1 && !(a.flags & kFlagNoAnchor)) ? 3 : 2;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (in_nat & (1u << q)) {
-      const int e = lane + kWave * q;
+    const bool nat_q = (in_nat & (1u << q)) != 0;
+    const int e = lane + kWave * q;
+    if (full ? valid[q] : nat_q)
       sm.c[slot][e] = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
-      atomicOr(&sm.flags[e], fl);
-    }
+    if (nat_q) atomicOr(&sm.flags[e], fl);
   }
   const bool any_nf = __ballot(nonfinite) != 0ull;
   if (lane == 0) {

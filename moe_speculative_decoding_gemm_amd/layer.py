@@ -56,6 +56,30 @@ class VerifyLayer:
                 active=torch.empty(E, dtype=torch.int32, device=dev),
                 stats=torch.zeros(L.STATS_BYTES, dtype=torch.uint8, device=dev))
 
+    def variant(self, **fields) -> "VerifyLayer":
+        """A layer on the same (already packed) weights whose shape differs in
+        the selection fields given (flags, fixed_budget, min_set,
+        reroute_budget), with its own workspace and output buffers."""
+        allowed = {"flags", "fixed_budget", "min_set", "reroute_budget"}
+        bad = set(fields) - allowed
+        if bad:
+            raise ValueError(f"variant() changes only {sorted(allowed)}, not {sorted(bad)}")
+        v = object.__new__(VerifyLayer)
+        v.shape = L.Shape.from_buffer_copy(self.shape)
+        for key, val in fields.items():
+            setattr(v.shape, key, val)
+        v.w = self.w
+        v.device = self.device
+        nbytes = L.acceptmoe_workspace_size(v.shape)
+        if nbytes == 0:
+            raise L.AcceptMoEError(L.EINVAL, "acceptmoe_workspace_size",
+                                   L.raw().acceptmoe_last_error().decode())
+        v.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        v.out = {key: torch.empty_like(t) for key, t in self.out.items()}
+        if "stats" in v.out:
+            v.out["stats"].zero_()
+        return v
+
     def run(self, x, parent, depth, commit, resident: Optional[torch.Tensor] = None,
             logits_in: Optional[torch.Tensor] = None, stream=None) -> dict:
         inputs = dict(self.w)

@@ -60,7 +60,7 @@ def _shape(m, **kw):
     (dict(n_depth=0), -1), (dict(min_set=129), -1), (dict(fixed_budget=-1), -1),
     (dict(reroute_budget=-2), -1), (dict(act_dtype=0, w_dtype=1), -2),
     (dict(act_dtype=2, w_dtype=2), -2), (dict(w_dtype=2, H=2048 + 64), -1),
-    (dict(flags=8), -2),
+    (dict(flags=64), -2),
 ])
 def test_shape_validation(m, kw, code):
     lib = m.raw()

@@ -237,3 +237,20 @@ def test_natural_mode_layer(lib):
     assert (out["topk_idx"].cpu().numpy() == O.natural_topk(lg, cfg.k)).all()
     assert st["n_active"] == st["n_natural_union"]
     assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("vname,flags,budget", [("MoE-Spec B=8", 16 | 32, 8),
+                                                ("full-softmax demand", 8, 0)])
+def test_selector_variant_layer(lib, vname, flags, budget):
+    """A selector variant through the whole layer: same kernels, output
+    within tolerance of the oracle's layer with the same flags."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=32, H=256, I=192, N=30, flags=flags,
+                                       fixed_budget=budget)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    for seed in range(2):
+        say(f"layer variant {vname} seed {seed}")
+        b = W.make_block(cfg, seed)
+        out, st = run_layer(lib, cfg, b, w)
+        ref = oracle_layer(cfg, b, w, out["logits_out"].cpu().numpy())
+        assert check_selection(out, ref, st, cfg, f"{vname} seed {seed}")
+        assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]

@@ -203,3 +203,35 @@ def test_permute_parity(lib, N, k, E):
         assert n == ref["n_active"]
         assert (active.cpu().numpy()[:n] == ref["active"]).all()
         assert (active.cpu().numpy()[n:] == -7).all()
+
+
+VARIANTS = [
+    ("full-softmax demand", 8, 0),
+    ("no anchor", 16, 0),
+    ("unit commitment", 32, 0),
+    ("MoE-Spec B=16", 16 | 32, 16),
+    ("MoE-Spec B=24", 16 | 32, 24),
+    ("AcceptMoE-B B=16", 0, 16),
+    ("full demand, no anchor", 8 | 16, 0),
+]
+
+
+@pytest.mark.parametrize("name,over", [("qwen3_30b", {}), ("gptoss_120b", {}),
+                                       ("dsv31", dict(E=64, H=256)),
+                                       ("qwen3_30b", dict(E=80, k=4, H=128, N=300))])
+@pytest.mark.parametrize("vname,flags,budget", VARIANTS)
+def test_selector_variants(lib, name, over, vname, flags, budget):
+    """Selector variants (flags on the same kernels) against the oracle with
+    the same flags: bit-exact sets, top-k and statistics."""
+    cfg = W.CONFIGS[name].with_(fixed_budget=budget, **over)
+    for seed in range(3):
+        say(f"variant {vname} on {name} {over} seed {seed}")
+        b = W.make_block(cfg, seed)
+        out, st = run_select(lib, cfg, b, flags=flags)
+        lg = out["logits_out"].cpu().numpy()
+        ref = oracle_select(cfg, b, logits_in=lg, flags=flags)
+        assert check_selection(out, ref, st, cfg, f"{vname} {name} seed {seed}")
+        if flags & 16:
+            assert st["n_anchor"] == 0
+        if budget and not (flags & 16) and cfg.resident_slots == 0:
+            assert st["n_eligible"] == max(budget, st["n_anchor"], cfg.k, cfg.min_set)
