@@ -86,6 +86,12 @@ struct GroupedArgs {
   // sorted_assign[t] of y_perm (token-major assignment order, i*k + j)
   // instead of row t
   int tok_rows;
+  // bf16 / fp8: work units per item (>= 1).  Unit r of an item runs its
+  // routed-row groups r, r + row_groups, ... (64 rows each), so an expert
+  // with many rows (the shared expert: all N tokens) spreads over more
+  // work-groups; the units of one item read the same weights at the same
+  // time.
+  int row_groups;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);

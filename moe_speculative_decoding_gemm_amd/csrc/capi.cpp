@@ -372,6 +372,8 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.num_cu = num_cu();
   a.packed = w_layout == ACCEPTMOE_LAYOUT_PACKED;
   a.tok_rows = 0;
+  // one expert (the shared expert) takes every row: spread its row groups
+  a.row_groups = E == 1 ? (N * k + 63) / 64 : 1;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -505,6 +507,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   // bf16 / fp8 weights: the down projection writes token-major rows, so the
   // combine gathers without inv_pos (same values, same arithmetic)
   g.tok_rows = g.w_kind != 0;
+  g.row_groups = 1;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
   rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
@@ -535,6 +538,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.y_perm = w.sh_y;
     gs.h_perm = w.sh_h;
     gs.tok_rows = 0;
+    gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
     if (rc) return rc;
   }

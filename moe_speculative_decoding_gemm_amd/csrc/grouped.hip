@@ -433,7 +433,9 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
   const uint16_t* src_base = static_cast<const uint16_t*>(GATEUP ? a.x : a.h_perm);
   const int src_ld = GATEUP ? H : I;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int R = a.row_groups > 1 ? a.row_groups : 1;
+  for (int unit = blockIdx.x; unit < n_items * R; unit += gridDim.x) {
+    const int item = unit % n_items, g0 = unit / n_items;
     const int u = item / tiles;
     const int tile = item - u * tiles;
     const int e = a.active[u];
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
                        (static_cast<size_t>(e) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
                        static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
 
-    for (int mg = 0; mg < te; mg += ROWS) {
+    for (int mg = g0 * ROWS; mg < te; mg += R * ROWS) {
       const int mt_n = min(MT, (te - mg + 15) >> 4);
       // Staging sources, PASSES rows per thread.  Rows past the routed ones
       // read row 0 of the group instead (their results are never stored), so
@@ -731,13 +733,14 @@ void launch_lds(const GroupedArgs& a, hipStream_t stream, int which) {
   static const int occ_g = resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED>, 2);
   static const int occ_d = resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED>, 2);
   const int max_active = a.E < a.N * a.k ? a.E : a.N * a.k;
+  const int R = a.row_groups > 1 ? a.row_groups : 1;
   if (which != 2) {
-    const int items = max_active * (2 * a.I / (64 * NT));
+    const int items = max_active * (2 * a.I / (64 * NT)) * R;
     const int grid = items < occ_g * a.num_cu ? items : occ_g * a.num_cu;
     expert_lds_kernel<WK, true, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
   }
   if (which != 1) {
-    const int items = max_active * (a.H / (64 * NT));
+    const int items = max_active * (a.H / (64 * NT)) * R;
     const int grid = items < occ_d * a.num_cu ? items : occ_d * a.num_cu;
     expert_lds_kernel<WK, false, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
   }

@@ -479,12 +479,47 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
     if (sm.bad[i]) sm.needy[atomicAdd(&sm.nneedy, 1)] = i;
   __syncthreads();
   const int nm = sm.nmem, nneedy = sm.nneedy;
-  // rank counting over (needy node, member) keys, rows padded to a multiple
-  // of 4 with key 0 (below every key), as many nodes per pass as fit
+  // Small sets: rank counting over (needy node, member) keys, rows padded to
+  // a multiple of 4 with key 0 (below every key), as many nodes per pass as
+  // fit.  Large sets (more than 64 members; the counting costs members^2 per
+  // node): one wave per needy node takes k rounds of a wave max over the
+  // keys of the eligible experts.  Both give each node's top-k keys in key
+  // order (value, then lower index).
   const int nmp = (nm + 3) & ~3;
+  if (nmp > 64) {
+    constexpr int NWV = kTail / kWave;
+    for (int c = wave; c < nneedy; c += NWV) {
+      const int i = sm.needy[c];
+      uint64_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + kWave * q;
+        const int ec = e < E ? e : E - 1;
+        const float v = lg_lds ? sm.lg[i * E + ec] : a.logits[static_cast<size_t>(i) * E + ec];
+        key[q] = (e < E && sm.set.elig[ec]) ? topk_key(v, ec) : 0ull;
+      }
+      for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
+        b = wave_max_u64(b);
+        const int ew = key_expert(b);
+        if ((ew & (kWave - 1)) == lane) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == (ew >> 6)) key[q] = 0ull;
+        }
+        if (lane == 0 && b != 0ull) {
+          sm.top_e[i * k + j] = ew;
+          sm.top_l[i * k + j] = key_logit(b);
+        }
+      }
+    }
+    __syncthreads();
+  }
   const int per = max(1, kKeyCap / max(nmp, 4));
   const float inv = 1.0f / static_cast<float>(max(nmp, 1));
-  for (int c0 = 0; c0 < nneedy; c0 += per) {
+  for (int c0 = 0; nmp <= 64 && c0 < nneedy; c0 += per) {
     const int cn = min(per, nneedy - c0);
     const int total = cn * nmp;
     for (int x = t; x < total; x += kTail) {
