@@ -31,6 +31,7 @@
 // applied to each 128-long partial sum.
 
 #include <type_traits>
+#include <utility>
 
 #include "amoe_common.h"
 #include "amoe_launch.h"
@@ -42,6 +43,16 @@ namespace {
 constexpr int kMT = 4;  // M tiles (16 rows each) per pass over the weights
 constexpr int kPackChunk = 128;  // reduction elements per packed chunk
 constexpr int kFragElems = 512;  // elements of one packed MFMA B fragment
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---- operand fragments --------------------------------------------------
 // 8 consecutive reduction elements of one row, as the MFMA wants them
@@ -405,8 +416,9 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const u32x2_t& u) {
   return f;
 }
 
+// FP8: two resident work-groups per CU (the register budget is cut to fit)
 template <int WK, bool GATEUP, int NT, int KC, bool PACKED>
-__global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
+__global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(GroupedArgs a) {
   static_assert(!PACKED || KC == kPackChunk, "packed weights come in 128-long chunks");
   constexpr int MT = 4;
   constexpr int ROWS = 16 * MT;
@@ -470,176 +482,192 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
                        static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
 
     for (int mg = g0 * ROWS; mg < te; mg += R * ROWS) {
-      const int mt_n = min(MT, (te - mg + 15) >> 4);
-      // Staging sources, PASSES rows per thread.  Rows past the routed ones
-      // read row 0 of the group instead (their results are never stored), so
-      // every load below is unconditional: guarded loads would make the
-      // compiler's wait counting fall back to waiting for all of them.
-      const uint16_t* src[PASSES];
-      const int kk = (t % TPR) * 8;
+      // One group of routed rows mg.. with MTV 16-row M tiles: only as many
+      // activation rows are staged (and MFMA tiles computed) as the group
+      // has, rounded up to 16, 32 or 64 -- rows past the routed ones would
+      // re-read row mg and still occupy the CU's load path.
+      auto group = [&](auto mtc) {
+        constexpr int MTV = decltype(mtc)::value;
+        constexpr int PV = 16 * MTV / RPP;  // staging passes
+        static_assert(RPP == 16 && PV == MTV, "one 16-row staging pass per M tile");
+        const int mt_n = min(MTV, (te - mg + 15) >> 4);
+        // Staging sources, PV rows per thread.  Rows past the routed ones
+        // read row 0 of the group instead (their results are never stored), so
+        // every load below is unconditional: guarded loads would make the
+        // compiler's wait counting fall back to waiting for all of them.
+        const uint16_t* src[PV];
+        const int kk = (t % TPR) * 8;
 #pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        const int rr = p * RPP + t / TPR;
-        const int m = mg + rr < te ? mg + rr : mg;
-        const int srcrow = GATEUP ? a.sorted_assign[off + m] / k : off + m;
-        src[p] = src_base + static_cast<size_t>(srcrow) * src_ld;
-      }
-      f32x4_t acc[NT][MT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-      // Pipeline, two chunks deep for both operands: activation chunk c waits
-      // in a VGPR ring of 2 until the end of chunk c-1, when it is written to
-      // LDS buffer c%2; weight chunk c waits in a VGPR ring of 2.  Issue order
-      // per chunk c: activations of c+2, compute c, weights of c+2, then store
-      // activations of c+1.  That store waits for activations c+1 and the
-      // loads older than them (vmcnt retires in issue order); weights c+1 were
-      // issued after activations c+1, so no wait ever stalls on weights that
-      // are not needed yet.  All loads of the steady state are unconditional;
-      // columns and steps past K are clamped to valid addresses whose data is
-      // never used.
-      u32x4_t sv[2][PASSES];
-      auto stage_load = [&](u32x4_t (&v)[PASSES], int c) {
-        const int k0 = min(c * KC + kk, K - 8);
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) v[p] = *reinterpret_cast<const u32x4_t*>(src[p] + k0);
-      };
-      auto stage_store = [&](const u32x4_t (&v)[PASSES], int buf) {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
+        for (int p = 0; p < PV; ++p) {
           const int rr = p * RPP + t / TPR;
-          *reinterpret_cast<u32x4_t*>(&sA[buf][rr * LDK + kk]) = v[p];
+          const int m = mg + rr < te ? mg + rr : mg;
+          const int srcrow = GATEUP ? a.sorted_assign[off + m] / k : off + m;
+          src[p] = src_base + static_cast<size_t>(srcrow) * src_ld;
         }
-      };
-      auto load_b = [&](BR (&b)[STEPS][NT], int c) {
+        f32x4_t acc[NT][MTV];
 #pragma unroll
-        for (int j = 0; j < STEPS; ++j) {
-          if (PACKED) {
-            const WTp* f = pbase + static_cast<size_t>((min(c, nchunks - 1) * 4 + j) * 4 * NT) * kFragElems;
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(f + nt * kFragElems));
-          } else {
-            const int s = min(c * STEPS + j, nsteps - 1);
+          for (int mt = 0; mt < MTV; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // Pipeline, two chunks deep for both operands: activation chunk c waits
+        // in a VGPR ring of 2 until the end of chunk c-1, when it is written to
+        // LDS buffer c%2; weight chunk c waits in a VGPR ring of 2.  Issue order
+        // per chunk c: activations of c+2, compute c, weights of c+2, then store
+        // activations of c+1.  That store waits for activations c+1 and the
+        // loads older than them (vmcnt retires in issue order); weights c+1 were
+        // issued after activations c+1, so no wait ever stalls on weights that
+        // are not needed yet.  All loads of the steady state are unconditional;
+        // columns and steps past K are clamped to valid addresses whose data is
+        // never used.
+        u32x4_t sv[2][PV];
+        auto stage_load = [&](u32x4_t (&v)[PV], int c) {
+          const int k0 = min(c * KC + kk, K - 8);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(wrow[nt] + s * 32));
+          for (int p = 0; p < PV; ++p) v[p] = *reinterpret_cast<const u32x4_t*>(src[p] + k0);
+        };
+        auto stage_store = [&](const u32x4_t (&v)[PV], int buf) {
+#pragma unroll
+          for (int p = 0; p < PV; ++p) {
+            const int rr = p * RPP + t / TPR;
+            *reinterpret_cast<u32x4_t*>(&sA[buf][rr * LDK + kk]) = v[p];
           }
-        }
-      };
-      auto compute = [&](const BR (&b)[STEPS][NT], int c, int buf) {
-        const int kb = (c * KC) >> 7;  // FP8 scale block (KC == 128 for FP8)
-        f32x4_t tmp[NT][MT];
-        if (WK == 2) {
+        };
+        // weights of chunk c, and for FP8 their block scales (one per tile row
+        // and 128-block: KC == 128), loaded together so that the scale is in a
+        // register when the chunk is computed
+        auto load_b = [&](BR (&b)[STEPS][NT], float (&bs)[NT], int c) {
+          if (WK == 2) {
+            const int kb = (min(c, nchunks - 1) * KC) >> 7;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) bs[nt] = scales[static_cast<size_t>(srow[nt]) * nkb + kb];
+          }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) tmp[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+          for (int j = 0; j < STEPS; ++j) {
+            if (PACKED) {
+              const WTp* f = pbase + static_cast<size_t>((min(c, nchunks - 1) * 4 + j) * 4 * NT) * kFragElems;
 #pragma unroll
-        for (int j = 0; j < STEPS; ++j) {
-          if (c * STEPS + j >= nsteps) break;
-          bf16x8_t bf[NT];
+              for (int nt = 0; nt < NT; ++nt)
+                b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(f + nt * kFragElems));
+            } else {
+              const int s = min(c * STEPS + j, nsteps - 1);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) bf[nt] = to_bf16x8(b[j][nt]);
+              for (int nt = 0; nt < NT; ++nt)
+                b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(wrow[nt] + s * 32));
+            }
+          }
+        };
+        auto compute = [&](const BR (&b)[STEPS][NT], const float (&bs)[NT], int c, int buf) {
+          f32x4_t tmp[NT][MTV];
+          if (WK == 2) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if (mt >= mt_n) break;
-            const bf16x8_t af = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(&sA[buf][(mt * 16 + r) * LDK + 32 * j + 8 * g]));
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int mt = 0; mt < MTV; ++mt) tmp[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int j = 0; j < STEPS; ++j) {
+            if (c * STEPS + j >= nsteps) break;
+            bf16x8_t bf[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bf[nt] = to_bf16x8(b[j][nt]);
+#pragma unroll
+            for (int mt = 0; mt < MTV; ++mt) {
+              if (mt >= mt_n) break;
+              const bf16x8_t af = __builtin_bit_cast(
+                  bf16x8_t, *reinterpret_cast<const u32x4_t*>(&sA[buf][(mt * 16 + r) * LDK + 32 * j + 8 * g]));
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) {
+                if (WK == 2)
+                  tmp[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], tmp[nt][mt], 0, 0, 0);
+                else
+                  acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], acc[nt][mt], 0, 0, 0);
+              }
+            }
+          }
+          if (WK == 2) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-              if (WK == 2)
-                tmp[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], tmp[nt][mt], 0, 0, 0);
-              else
-                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nt], acc[nt][mt], 0, 0, 0);
+              const float sc = bs[nt];
+#pragma unroll
+              for (int mt = 0; mt < MTV; ++mt) acc[nt][mt] += sc * tmp[nt][mt];
+            }
+          }
+        };
+
+        // Weight chunks in flight: 2 for bf16, 4 for fp8 (an fp8 chunk is half
+        // the bytes; a CU streams at the rate its bytes in flight allow).
+        constexpr int DW = WK == 2 ? 4 : 2;
+        BR bq[DW][STEPS][NT];
+        float bsc[DW][NT];  // FP8 block scales of the chunks in flight
+        // prologue: A0 B0 A1 B1 .. B(DW-1)
+        stage_load(sv[0], 0);
+        load_b(bq[0], bsc[0], 0);
+        stage_load(sv[1], min(1, nchunks - 1));
+#pragma unroll
+        for (int d = 1; d < DW; ++d) load_b(bq[d], bsc[d], min(d, nchunks - 1));
+        // down, token-major output: each routed row's assignment index, loaded
+        // behind the pipeline's loads and used only by the epilogue
+        const bool tok = !GATEUP && a.tok_rows;
+        int my_row = 0;
+        if (tok) my_row = a.sorted_assign[off + min(mg + lane, te - 1)];
+        stage_store(sv[0], 0);
+        __syncthreads();
+        // chunk c: weights in ring slot c % DW, activations in VGPR ring / LDS
+        // buffer c % 2.  guard: near the end, loads past the last chunk are
+        // skipped (the steady state has none).
+        auto body = [&](auto wc, int c, bool guard) {
+          constexpr int w = decltype(wc)::value;
+          constexpr int i = w & 1;
+          if (!guard || c + 2 < nchunks) stage_load(sv[i], c + 2);
+          compute(bq[w], bsc[w], c, i);
+          if (!guard || c + DW < nchunks) load_b(bq[w], bsc[w], c + DW);
+          if (!guard || c + 1 < nchunks) stage_store(sv[i ^ 1], i ^ 1);
+          __syncthreads();
+        };
+        int c = 0;
+        for (; c + 2 * DW <= nchunks; c += DW)  // every load of these DW chunks is in range
+          static_for<DW>([&](auto d) { body(d, c + decltype(d)::value, false); });
+        // 0 .. 2*DW-1 chunks remain; c is a multiple of DW
+        static_for<2 * DW>([&](auto q) {
+          constexpr int qq = decltype(q)::value;
+          if (c + qq < nchunks) body(std::integral_constant<int, qq % DW>{}, c + qq, true);
+        });
+
+        if (tok) {
+          if (t < ROWS) s_row[t] = my_row;
+          __syncthreads();
+        }
+        // epilogue: lane (r, g) holds D[m = 4g + j][n = r] of each tile
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int mt = 0; mt < MTV; ++mt) {
+            if (mt >= mt_n) break;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int m = mg + 16 * mt + 4 * g + j;
+              const float v = acc[nt][mt][j];
+              if (GATEUP) {
+                const float up = __shfl_xor(v, 8, kWave);
+                if (half == 0 && m < te)
+                  static_cast<uint16_t*>(a.h_perm)[static_cast<size_t>(off + m) * I + orow[nt]] =
+                      f32_to_bf16(silu(v) * up);
+              } else if (m < te) {
+                const int row = tok ? s_row[m - mg] : off + m;
+                a.y_perm[static_cast<size_t>(row) * H + orow[nt]] = v;
+              }
             }
           }
         }
-        if (WK == 2) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float sc = scales[static_cast<size_t>(srow[nt]) * nkb + kb];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += sc * tmp[nt][mt];
-          }
-        }
       };
-
-      BR bq[2][STEPS][NT];
-      // prologue: A0 B0 A1 B1
-      stage_load(sv[0], 0);
-      load_b(bq[0], 0);
-      stage_load(sv[1], min(1, nchunks - 1));
-      load_b(bq[1], min(1, nchunks - 1));
-      // down, token-major output: each routed row's assignment index, loaded
-      // behind the pipeline's loads and used only by the epilogue
-      const bool tok = !GATEUP && a.tok_rows;
-      int my_row = 0;
-      if (tok) my_row = a.sorted_assign[off + min(mg + lane, te - 1)];
-      stage_store(sv[0], 0);
-      __syncthreads();
-      auto body_main = [&](auto ic, int c) {
-        constexpr int i = decltype(ic)::value;
-        stage_load(sv[i], c + 2);
-        compute(bq[i], c, i);
-        load_b(bq[i], c + 2);
-        stage_store(sv[i ^ 1], i ^ 1);
-        __syncthreads();
-      };
-      auto body_tail = [&](auto ic, int c) {
-        constexpr int i = decltype(ic)::value;
-        if (c + 2 < nchunks) stage_load(sv[i], c + 2);
-        compute(bq[i], c, i);
-        if (c + 2 < nchunks) load_b(bq[i], c + 2);
-        if (c + 1 < nchunks) stage_store(sv[i ^ 1], i ^ 1);
-        __syncthreads();
-      };
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, 1>;
-      int c = 0;
-      for (; c + 4 <= nchunks; c += 2) {  // chunks c, c+1 both prefetch (c+3 < nchunks)
-        body_main(I0{}, c);
-        body_main(I1{}, c + 1);
-      }
-      // 0..3 chunks remain; c is even
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (c + q >= nchunks) break;
-        if ((q & 1) == 0)
-          body_tail(I0{}, c + q);
-        else
-          body_tail(I1{}, c + q);
-      }
-
-      if (tok) {
-        if (t < ROWS) s_row[t] = my_row;
-        __syncthreads();
-      }
-      // epilogue: lane (r, g) holds D[m = 4g + j][n = r] of each tile
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (mt >= mt_n) break;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int m = mg + 16 * mt + 4 * g + j;
-            const float v = acc[nt][mt][j];
-            if (GATEUP) {
-              const float up = __shfl_xor(v, 8, kWave);
-              if (half == 0 && m < te)
-                static_cast<uint16_t*>(a.h_perm)[static_cast<size_t>(off + m) * I + orow[nt]] =
-                    f32_to_bf16(silu(v) * up);
-            } else if (m < te) {
-              const int row = tok ? s_row[m - mg] : off + m;
-              a.y_perm[static_cast<size_t>(row) * H + orow[nt]] = v;
-            }
-          }
-        }
-      }
+      const int rows = te - mg;
+      if (rows <= 16)
+        group(std::integral_constant<int, 1>{});
+      else if (rows <= 32)
+        group(std::integral_constant<int, 2>{});
+      else
+        group(std::integral_constant<int, 4>{});
     }
   }
 }
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(256) void expert_lds_kernel(GroupedArgs a) {
 //   [expert][group][chunk of 128][step (4)][wave (4)][tile nt (NT)][lane][8]
 // The reduction dimension is zero-padded to whole chunks.
 constexpr int kPackNT_bf16 = 1;
-constexpr int kPackNT_fp8 = 2;
+constexpr int kPackNT_fp8 = 1;
 
 template <int WK, bool GATEUP>
 __global__ __launch_bounds__(256) void pack_kernel(const typename WeightT<WK>::T* __restrict__ src,
@@ -761,7 +789,7 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which) {
       if (a.packed)
         launch_lds<2, kPackNT_fp8, kPackChunk, true>(a, stream, which);
       else
-        launch_lds<2, 2, 128, false>(a, stream, which);
+        launch_lds<2, 1, 128, false>(a, stream, which);
       break;
   }
   return hipGetLastError();
