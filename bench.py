@@ -53,6 +53,9 @@ def parse():
                     help="skip the selector-variant comparison (natural routing, AcceptMoE-B, "
                          "MoE-Spec, full-softmax demand on the same kernels and blocks)")
     ap.add_argument("--variant-steps", type=int, default=200)
+    ap.add_argument("--moesd-sweep", action="store_true",
+                    help="instead of the headline run: natural-routing layer time T(B, gamma) for "
+                         "B sequences x gamma-token chains, and eta(B, gamma) = T(B,1)/T(B,gamma)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--flags", type=int, default=None, help="override shape flags (1 = natural)")
     ap.add_argument("--fixed-budget", type=int, default=None)
@@ -77,6 +80,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.moesd_sweep:
+        moesd_sweep(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -322,6 +328,85 @@ def measured_traffic(workload):
     if sha != rec.get("grouped_hip_sha256"):
         return None
     return rec["bytes_per_launch"]
+
+
+def moesd_sweep(args):
+    """[MoESD §5.2, §5.3]: target efficiency eta(B, gamma) = T(B, 1) / T(B, gamma)
+    of the MoE layer alone, natural routing (standard speculative decoding),
+    for B sequences each verifying a chain of gamma tokens (N = B * gamma),
+    on this library's kernels; next to each point the measured number of
+    active experts and MoESD's uniform-routing estimate E(1 - (1 - k/E)^N)."""
+    import torch
+    import moe_speculative_decoding_gemm_amd as M
+    import workloads as W
+    from workloads.gen import _CHAIN8_COMMIT
+    dev = torch.device("cuda:0")
+    base = W.CONFIGS[args.config].with_(tree="chains", commit=_CHAIN8_COMMIT,
+                                        flags=M.F_NATURAL, resident_slots=0, shared=False)
+    DT = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3FN}
+    first = base.with_(N=8, n_chains=8, chain_len=1)
+    shape = M.make_shape(first.N, base.H, base.I, base.E, base.k, base.n_depth,
+                         act_dtype=DT[base.act], w_dtype=DT[base.w], flags=base.flags)
+    ew = W.expert_weights(base, layer=0, device=dev)
+    b0 = W.make_block(first, 0)
+    layer0 = M.VerifyLayer(shape, dict(w_router=b0.w_router.to(dev),
+                                       b_router=None if b0.b_router is None else b0.b_router.to(dev),
+                                       w13=ew["w13"], w2=ew["w2"], s13=ew["s13"], s2=ew["s2"]),
+                           device=dev)
+    points = []
+    Bs = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+    gammas = [1, 2, 4, 8]
+    for B in Bs:
+        for gmm in gammas:
+            N = B * gmm
+            if N > 4096:
+                continue
+            cfg = base.with_(N=N, n_chains=B, chain_len=gmm)
+            layer = layer0.variant(N=N)
+            blocks = []
+            for seed in range(2):
+                b = W.make_block(cfg, seed)
+                blocks.append(dict(x=b.x.to(dev), parent=torch.from_numpy(b.parent).to(dev),
+                                   depth=torch.from_numpy(b.depth).to(dev),
+                                   commit=torch.from_numpy(b.commit).to(dev)))
+            us_list, U = [], []
+            for d in blocks:
+                out = layer.run(d["x"], d["parent"], d["depth"], d["commit"])
+                torch.cuda.synchronize()
+                U.append(M.decode_stats(out["stats"])["n_active"])
+                g = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream()
+                cap.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(cap):
+                    layer.run(d["x"], d["parent"], d["depth"], d["commit"])
+                torch.cuda.current_stream().wait_stream(cap)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    layer.run(d["x"], d["parent"], d["depth"], d["commit"])
+                g.replay()
+                torch.cuda.synchronize()
+                reps = 20 if N <= 1024 else 5
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us_list.append(e0.elapsed_time(e1) * 1e3 / reps)
+                del g
+            t_us = statistics.mean(us_list)
+            u_model = base.E * (1.0 - (1.0 - base.k / base.E) ** N)
+            points.append({"B": B, "gamma": gmm, "N": N, "us": round(t_us, 2),
+                           "U": statistics.mean(U), "U_uniform_model": round(u_model, 2)})
+            log(f"B={B} gamma={gmm} N={N}: {t_us:.1f} us, U={statistics.mean(U):.1f} "
+                f"(uniform model {u_model:.1f})")
+    t1 = {p["B"]: p["us"] for p in points if p["gamma"] == 1}
+    for p in points:
+        p["eta"] = round(t1[p["B"]] / p["us"], 4) if p["B"] in t1 else None
+    print(json.dumps({"sweep": "moesd_target_efficiency", "workload": f"{base.name}: E={base.E} "
+                      f"k={base.k} H={base.H} I={base.I}, {base.w} experts, natural routing, "
+                      "B chains of gamma tokens", "points": points}), flush=True)
 
 
 def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):

@@ -58,9 +58,9 @@ class VerifyLayer:
 
     def variant(self, **fields) -> "VerifyLayer":
         """A layer on the same (already packed) weights whose shape differs in
-        the selection fields given (flags, fixed_budget, min_set,
+        the fields given (N, n_depth, flags, fixed_budget, min_set,
         reroute_budget), with its own workspace and output buffers."""
-        allowed = {"flags", "fixed_budget", "min_set", "reroute_budget"}
+        allowed = {"N", "n_depth", "flags", "fixed_budget", "min_set", "reroute_budget"}
         bad = set(fields) - allowed
         if bad:
             raise ValueError(f"variant() changes only {sorted(allowed)}, not {sorted(bad)}")
@@ -75,7 +75,13 @@ class VerifyLayer:
             raise L.AcceptMoEError(L.EINVAL, "acceptmoe_workspace_size",
                                    L.raw().acceptmoe_last_error().decode())
         v.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
-        v.out = {key: torch.empty_like(t) for key, t in self.out.items()}
+        N = v.shape.N
+        v.out = {}
+        for key, t in self.out.items():
+            shp = list(t.shape)
+            if key in ("y", "logits_out", "topk_idx", "topk_gate"):
+                shp[0] = N
+            v.out[key] = torch.empty(shp, dtype=t.dtype, device=self.device)
         if "stats" in v.out:
             v.out["stats"].zero_()
         return v
