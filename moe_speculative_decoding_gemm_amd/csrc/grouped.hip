@@ -426,7 +426,6 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
   constexpr int LDK = KC + 8;         // LDS row stride in bf16 elements (16 B pad)
   constexpr int TPR = KC / 8;         // threads per staged row, 16 B each
   constexpr int RPP = 256 / TPR;      // staged rows per pass
-  constexpr int PASSES = ROWS / RPP;
   using WTp = typename WeightT<WK>::T;
   using BR = typename BRaw<WK>::T;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * LDK];

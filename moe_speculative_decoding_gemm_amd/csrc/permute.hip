@@ -69,7 +69,10 @@ __global__ __launch_bounds__(256) void combine_kernel(int N, int k, int H,
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (j < k) acc += g[j] * v[j];
+    if (j < k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(g[j], v[j][q], acc[q]);
+    }
   if (y_shared) acc += *reinterpret_cast<const f32x4_t*>(y_shared + static_cast<size_t>(i) * H + h);
   if (kBf16) {
     u32x2_t o;
