@@ -294,9 +294,92 @@ enum {
   ACCEPTMOE_STAGE_GATEUP = 3,   /* routed experts: gate/up projections + SwiGLU             */
   ACCEPTMOE_STAGE_DOWN = 4,     /* routed experts: down projection                          */
   ACCEPTMOE_STAGE_EXPERTS = 5,  /* routed experts: both projections                         */
-  ACCEPTMOE_STAGE_COMBINE = 6   /* shared expert (if any) + unpermute/combine               */
+  ACCEPTMOE_STAGE_COMBINE = 6,  /* shared expert (if any) + unpermute/combine               */
+  ACCEPTMOE_STAGE_FETCH = 7     /* verify_block_cached: host-to-device expert copies        */
 };
 int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop);
+
+/* ---------------------------------------------------------------------------
+ * Physical expert offload: a per-layer cache of device expert slots.
+ *
+ * [AcceptMoE news §02]: under offload an expert that is already on the GPU
+ * runs at once and one that is not has to be loaded from CPU memory first;
+ * residency-aware pruning drops low-demand non-resident experts from the
+ * eligible set.  [AcceptMoE news §03]: 48 expert slots per layer; the
+ * measures are host-to-device expert bytes and the expert-cache hit rate.
+ * The pages give no replacement policy; this one is least recently used.
+ *
+ * The caller keeps every expert's packed weights (acceptmoe_pack_experts
+ * layout) in host memory -- pinned (hipHostMalloc) for asynchronous DMA --
+ * and owns n_slots + n_spill device slots of packed weights.  Slots
+ * 0..n_slots-1 are persistent: their experts form the resident set.  The
+ * spill slots hold experts that miss when every persistent slot holds an
+ * expert of the same block; they are loaded again on their next use.
+ *
+ * acceptmoe_cache_state (host memory, owned by the caller; zero counters and
+ * clock, slot_expert / expert_slot -1 and resident 0 for an empty cache, or
+ * fill a warm start consistently: slot_expert[q] = e <=> expert_slot[e] = q,
+ * resident[e] = 1).
+ *
+ * acceptmoe_cache_plan (host only, no GPU): for the ascending active expert
+ * ids of one block, hits keep their slot and take the current clock; each
+ * miss, in ascending expert order, takes the lowest empty persistent slot,
+ * else evicts the least recently used persistent slot whose expert is not
+ * active in this block (ties: lowest slot), else takes the next spill slot
+ * n_slots + j.  Writes the fetches (expert, slot) in that order and updates
+ * the state and its counters.  ACCEPTMOE_EINVAL (state unchanged) when the
+ * misses need more than n_spill spill slots, or for a malformed state /
+ * active list (ids outside [0, E) or repeated).
+ *
+ * verify_block_cached: verify_block with the routed experts' weights taken
+ * from the cache.  The selection's resident mask is cache->dev_resident (so
+ * ACCEPTMOE residency-aware pruning applies when reroute_budget > 0); the
+ * active experts are copied back to the host and the stream is synchronized
+ * once; the plan's missing experts are copied host -> device into their
+ * slots with hipMemcpyAsync on `stream`, followed by dev_expert_slot and
+ * dev_resident; then the expert kernels read expert e's weights from slot
+ * dev_expert_slot[e].  in->w13, in->w2 and in->resident are not used; FP8
+ * scales (in->s13, in->s2, all E experts) and the shared expert stay on the
+ * device.  Packed BF16 or FP8 weights only (else ACCEPTMOE_ENOTSUP).  Not
+ * capturable in a HIP graph (it synchronizes).  The state's tables must not
+ * change while the call's copies are pending on the stream.  report (host,
+ * may be NULL) receives this call's counts.
+ * ------------------------------------------------------------------------- */
+typedef struct acceptmoe_cache_state {
+  int32_t E;              /* routed experts                                      */
+  int32_t n_slots;        /* persistent device slots                             */
+  int32_t n_spill;        /* spill slots after them                              */
+  int32_t _pad;
+  int32_t* slot_expert;   /* [n_slots] expert held, -1 = empty                   */
+  int32_t* expert_slot;   /* [E] slot (persistent or spill) for the last block, -1 = none */
+  uint8_t* resident;      /* [E] 1 iff the expert holds a persistent slot        */
+  int64_t* last_use;      /* [n_slots] clock of the slot's last use              */
+  int64_t clock;          /* blocks planned                                      */
+  int64_t hits, misses, spills, h2d_bytes;  /* running totals                    */
+} acceptmoe_cache_state;
+
+typedef struct acceptmoe_expert_cache {
+  acceptmoe_cache_state* state;   /* host                                          */
+  const void* host_w13;           /* host, packed w13 of all E experts             */
+  const void* host_w2;            /* host, packed w2 of all E experts              */
+  void* dev_w13;                  /* device, packed w13 of n_slots + n_spill slots */
+  void* dev_w2;                   /* device, packed w2 of n_slots + n_spill slots  */
+  int32_t* dev_expert_slot;       /* device [E]                                    */
+  uint8_t* dev_resident;          /* device [E]                                    */
+} acceptmoe_expert_cache;
+
+typedef struct acceptmoe_cache_report {  /* one verify_block_cached call      */
+  int32_t n_active, n_hits, n_fetched, n_spilled;
+  int64_t h2d_bytes;
+} acceptmoe_cache_report;
+
+int acceptmoe_cache_plan(acceptmoe_cache_state* state, const int32_t* active /* host */,
+                         int32_t n_active, int32_t* fetch_expert /* host [n_active] */,
+                         int32_t* fetch_slot /* host [n_active] */, int32_t* n_fetch);
+int verify_block_cached(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
+                        const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
+                        acceptmoe_cache_report* report, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Messages and version (host). */
 const char* acceptmoe_strerror(int code);

@@ -55,6 +55,28 @@ class Outputs(C.Structure):
         "y", "logits_out", "eligible", "topk_idx", "topk_gate", "counts", "active", "stats")]
 
 
+class CacheState(C.Structure):
+    _fields_ = [("E", C.c_int32), ("n_slots", C.c_int32), ("n_spill", C.c_int32),
+                ("_pad", C.c_int32), ("slot_expert", C.c_void_p), ("expert_slot", C.c_void_p),
+                ("resident", C.c_void_p), ("last_use", C.c_void_p), ("clock", C.c_int64),
+                ("hits", C.c_int64), ("misses", C.c_int64), ("spills", C.c_int64),
+                ("h2d_bytes", C.c_int64)]
+
+
+class ExpertCacheDesc(C.Structure):
+    _fields_ = [("state", C.c_void_p), ("host_w13", C.c_void_p), ("host_w2", C.c_void_p),
+                ("dev_w13", C.c_void_p), ("dev_w2", C.c_void_p),
+                ("dev_expert_slot", C.c_void_p), ("dev_resident", C.c_void_p)]
+
+
+class CacheReport(C.Structure):
+    _fields_ = [("n_active", C.c_int32), ("n_hits", C.c_int32), ("n_fetched", C.c_int32),
+                ("n_spilled", C.c_int32), ("h2d_bytes", C.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 STATS_BYTES = 48
 _STATS_FIELDS = ("n_anchor", "n_selfsize", "n_eligible", "n_pruned", "n_active",
                  "n_active_nonresident", "n_natural_union", "err_flags", "r_eff",
@@ -79,6 +101,8 @@ def _load():
         "moe_combine": (C.c_int, [i32] * 4 + [vp] * 5 + [vp]),
         "acceptmoe_workspace_size": (sz, [vp]),
         "verify_block": (C.c_int, [vp, vp, vp, vp, sz, vp]),
+        "acceptmoe_cache_plan": (C.c_int, [vp, vp, i32, vp, vp, vp]),
+        "verify_block_cached": (C.c_int, [vp, vp, vp, vp, vp, vp, sz, vp]),
         "acceptmoe_set_stage_timer": (C.c_int, [i32, vp, vp]),
         "acceptmoe_strerror": (C.c_char_p, [C.c_int]),
         "acceptmoe_last_error": (C.c_char_p, []),
@@ -95,7 +119,8 @@ _lib = _load()
 EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "acceptmoe_packed_size", "acceptmoe_pack_experts",
-            "acceptmoe_workspace_size", "verify_block", "acceptmoe_set_stage_timer",
+            "acceptmoe_workspace_size", "verify_block", "acceptmoe_cache_plan",
+            "verify_block_cached", "acceptmoe_set_stage_timer",
             "acceptmoe_strerror",
             "acceptmoe_last_error", "acceptmoe_version")
 
@@ -106,7 +131,7 @@ def raw():
 
 
 STAGE_NONE, STAGE_SELECT, STAGE_PERMUTE, STAGE_GATEUP, STAGE_DOWN, STAGE_EXPERTS, \
-    STAGE_COMBINE = range(7)
+    STAGE_COMBINE, STAGE_FETCH = range(8)
 
 
 def acceptmoe_set_stage_timer(stage: int, start_event, stop_event):
@@ -290,8 +315,7 @@ def acceptmoe_workspace_size(shape: Shape) -> int:
     return int(_lib.acceptmoe_workspace_size(C.byref(shape)))
 
 
-def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
-    """inputs/outputs: dicts keyed like acceptmoe_inputs / acceptmoe_outputs."""
+def _block_args(shape: Shape, inputs: dict, outputs: dict):
     N, H, I, E, k = shape.N, shape.H, shape.I, shape.E, shape.k
     adt = _act_dt(shape)
     packed = shape.w_layout == LAYOUT_PACKED
@@ -323,6 +347,38 @@ def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
         _ptr(o("counts"), "counts", torch.int32, (E,)),
         _ptr(o("active"), "active", torch.int32, (E,)),
         _ptr(o("stats"), "stats", torch.uint8, (STATS_BYTES,)))
+    return inp, out
+
+
+def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
+    """inputs/outputs: dicts keyed like acceptmoe_inputs / acceptmoe_outputs."""
+    inp, out = _block_args(shape, inputs, outputs)
     _check(_lib.verify_block(C.byref(shape), C.byref(inp), C.byref(out),
                              _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0,
                              _stream(stream)), "verify_block")
+
+
+def acceptmoe_cache_plan(state: CacheState, active) -> list:
+    """Host-only fetch plan for one block's ascending active expert ids (a
+    sequence of ints); updates `state` and returns [(expert, slot), ...]."""
+    act = (C.c_int32 * max(1, len(active)))(*[int(a) for a in active])
+    fe = (C.c_int32 * max(1, len(active)))()
+    fs = (C.c_int32 * max(1, len(active)))()
+    nf = C.c_int32(0)
+    _check(_lib.acceptmoe_cache_plan(C.byref(state), act, len(active), fe, fs, C.byref(nf)),
+           "acceptmoe_cache_plan")
+    return [(fe[i], fs[i]) for i in range(nf.value)]
+
+
+def verify_block_cached(shape: Shape, inputs: dict, cache: ExpertCacheDesc, outputs: dict, ws,
+                        stream=None) -> dict:
+    """verify_block with the routed experts from `cache` (in inputs, w13 / w2 /
+    resident are not used).  Synchronizes the stream once; returns the call's
+    report as a dict."""
+    inp, out = _block_args(shape, inputs, outputs)
+    report = CacheReport()
+    _check(_lib.verify_block_cached(C.byref(shape), C.byref(inp), C.byref(cache), C.byref(out),
+                                    C.byref(report), _ptr(ws, "ws", torch.uint8),
+                                    ws.numel() if ws is not None else 0, _stream(stream)),
+           "verify_block_cached")
+    return report.as_dict()

@@ -234,6 +234,166 @@ int w_kind(int w_dtype) {
   return w_dtype == ACCEPTMOE_F32 ? 0 : (w_dtype == ACCEPTMOE_BF16 ? 1 : 2);
 }
 
+// ------------------------------------------------------------ expert cache --
+int check_state(const acceptmoe_cache_state* st) {
+  if (!st) return fail(ACCEPTMOE_EINVAL, "cache state is NULL");
+  if (st->E < 1 || st->E > 256 || st->n_slots < 0 || st->n_slots > st->E || st->n_spill < 0 ||
+      st->n_spill > st->E)
+    return fail(ACCEPTMOE_EINVAL, "cache state: E=%d, n_slots=%d, n_spill=%d out of range", st->E,
+                st->n_slots, st->n_spill);
+  if (!st->slot_expert || !st->expert_slot || !st->resident || !st->last_use)
+    return fail(ACCEPTMOE_EINVAL, "cache state: a table pointer is NULL");
+  for (int q = 0; q < st->n_slots; ++q) {
+    const int e = st->slot_expert[q];
+    if (e < -1 || e >= st->E || (e >= 0 && (st->expert_slot[e] != q || !st->resident[e])))
+      return fail(ACCEPTMOE_EINVAL, "cache state: slot %d holds expert %d inconsistently", q, e);
+  }
+  return ACCEPTMOE_OK;
+}
+
+// The fetch plan for one block's active experts (ascending ids).  Hits keep
+// their slot and take the current clock.  Each miss, in ascending expert
+// order, takes the lowest empty persistent slot, else evicts the least
+// recently used persistent slot whose expert is not active in this block
+// (ties: lowest slot), else a spill slot n_slots + j (held for this block
+// only, not resident afterwards).  The whole plan is checked before the
+// state changes: too few spill slots leaves it untouched.
+int plan_fetches(acceptmoe_cache_state* st, const int32_t* active, int n_active,
+                 int32_t* fetch_expert, int32_t* fetch_slot, int32_t* n_fetch,
+                 acceptmoe_cache_report* rep) {
+  const int E = st->E, S = st->n_slots;
+  uint8_t act[256];
+  std::memset(act, 0, sizeof(act));
+  int misses = 0;
+  for (int u = 0; u < n_active; ++u) {
+    const int e = active[u];
+    if (e < 0 || e >= E || act[e]) return fail(ACCEPTMOE_EINVAL, "bad active expert %d", e);
+    act[e] = 1;
+    if (!st->resident[e]) ++misses;
+  }
+  int free_or_evictable = 0;
+  for (int q = 0; q < S; ++q) {
+    const int e = st->slot_expert[q];
+    if (e < 0 || !act[e]) ++free_or_evictable;
+  }
+  const int spill = misses > free_or_evictable ? misses - free_or_evictable : 0;
+  if (spill > st->n_spill)
+    return fail(ACCEPTMOE_EINVAL, "%d active experts miss the cache; %d slots and %d spill slots "
+                "cannot hold them", misses, free_or_evictable, st->n_spill);
+  st->clock += 1;
+  // a spill slot holds its expert for one block only
+  for (int e = 0; e < E; ++e)
+    if (!st->resident[e]) st->expert_slot[e] = -1;
+  int nf = 0, hits = 0, spilled = 0;
+  for (int u = 0; u < n_active; ++u) {
+    const int e = active[u];
+    if (st->resident[e]) {
+      st->last_use[st->expert_slot[e]] = st->clock;
+      ++hits;
+      continue;
+    }
+    int slot = -1;
+    for (int q = 0; q < S && slot < 0; ++q)
+      if (st->slot_expert[q] < 0) slot = q;
+    if (slot < 0) {
+      for (int q = 0; q < S; ++q) {
+        const int o = st->slot_expert[q];
+        if (o < 0 || act[o]) continue;
+        if (slot < 0 || st->last_use[q] < st->last_use[slot]) slot = q;
+      }
+    }
+    if (slot >= 0) {
+      const int old = st->slot_expert[slot];
+      if (old >= 0) {
+        st->resident[old] = 0;
+        st->expert_slot[old] = -1;
+      }
+      st->slot_expert[slot] = e;
+      st->resident[e] = 1;
+      st->last_use[slot] = st->clock;
+    } else {
+      slot = S + spilled++;
+    }
+    st->expert_slot[e] = slot;
+    fetch_expert[nf] = e;
+    fetch_slot[nf] = slot;
+    ++nf;
+  }
+  *n_fetch = nf;
+  st->hits += hits;
+  st->misses += nf;
+  st->spills += spilled;
+  if (rep) {
+    rep->n_active = n_active;
+    rep->n_hits = hits;
+    rep->n_fetched = nf;
+    rep->n_spilled = spilled;
+    rep->h2d_bytes = 0;
+  }
+  return ACCEPTMOE_OK;
+}
+
+int check_cache(const acceptmoe_shape* s, const acceptmoe_expert_cache* c) {
+  if (s->w_layout != ACCEPTMOE_LAYOUT_PACKED || s->w_dtype == ACCEPTMOE_F32)
+    return fail(ACCEPTMOE_ENOTSUP, "the expert cache holds packed BF16 or FP8 weights");
+  int rc = check_state(c->state);
+  if (rc) return rc;
+  if (c->state->E != s->E)
+    return fail(ACCEPTMOE_EINVAL, "cache state E=%d != shape E=%d", c->state->E, s->E);
+  if (!c->host_w13 || !c->host_w2 || !c->dev_w13 || !c->dev_w2 || !c->dev_expert_slot ||
+      !c->dev_resident)
+    return fail(ACCEPTMOE_EINVAL, "a cache pointer is NULL");
+  return ACCEPTMOE_OK;
+}
+
+// After the selection: read the active experts back (one stream
+// synchronization), plan, copy the missing experts' packed weights from
+// host memory into their slots, then the slot table and resident mask.
+int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const int32_t* active,
+                const int32_t* n_active, acceptmoe_cache_report* report, hipStream_t stream) {
+  acceptmoe_cache_state* st = c->state;
+  int32_t host_n = 0;
+  int32_t host_active[256];
+  int32_t fe[256], fs[256];
+  hipError_t e = hipMemcpyAsync(&host_n, n_active, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host_active, active, sizeof(int32_t) * s->E, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  int rc = hip_status(e, "verify_block_cached/read active experts");
+  if (rc) return rc;
+  if (host_n < 0 || host_n > s->E)
+    return fail(ACCEPTMOE_EINVAL, "verify_block_cached: device reported %d active experts", host_n);
+  acceptmoe_cache_report rep;
+  int nf = 0;
+  rc = plan_fetches(st, host_active, host_n, fe, fs, &nf, &rep);
+  if (rc) return rc;
+  const int wk = w_kind(s->w_dtype);
+  const size_t b13 = amoe::packed_bytes(0, wk, 1, s->H, s->I);
+  const size_t b2 = amoe::packed_bytes(1, wk, 1, s->H, s->I);
+  const char* h13 = static_cast<const char*>(c->host_w13);
+  const char* h2 = static_cast<const char*>(c->host_w2);
+  char* d13 = static_cast<char*>(c->dev_w13);
+  char* d2 = static_cast<char*>(c->dev_w2);
+  timer_mark(ACCEPTMOE_STAGE_FETCH, true, stream);
+  for (int f = 0; f < nf && e == hipSuccess; ++f) {
+    e = hipMemcpyAsync(d13 + b13 * fs[f], h13 + b13 * fe[f], b13, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d2 + b2 * fs[f], h2 + b2 * fe[f], b2, hipMemcpyHostToDevice, stream);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->dev_expert_slot, st->expert_slot, sizeof(int32_t) * s->E,
+                       hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->dev_resident, st->resident, s->E, hipMemcpyHostToDevice, stream);
+  timer_mark(ACCEPTMOE_STAGE_FETCH, false, stream);
+  rc = hip_status(e, "verify_block_cached/fetch");
+  if (rc) return rc;
+  rep.h2d_bytes = static_cast<int64_t>(nf) * static_cast<int64_t>(b13 + b2);
+  st->h2d_bytes += rep.h2d_bytes;
+  if (report) *report = rep;
+  return ACCEPTMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,7 +418,7 @@ const char* acceptmoe_strerror(int code) {
 }
 
 int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop) {
-  if (stage < ACCEPTMOE_STAGE_NONE || stage > ACCEPTMOE_STAGE_COMBINE)
+  if (stage < ACCEPTMOE_STAGE_NONE || stage > ACCEPTMOE_STAGE_FETCH)
     return fail(ACCEPTMOE_EINVAL, "unknown stage %d", stage);
   g_timer_stage = (start && stop) ? stage : 0;
   g_timer_start = start;
@@ -374,6 +534,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.tok_rows = 0;
   // one expert (the shared expert) takes every row: spread its row groups
   a.row_groups = E == 1 ? (N * k + 63) / 64 : 1;
+  a.w_slot = nullptr;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -430,16 +591,26 @@ size_t acceptmoe_workspace_size(const acceptmoe_shape* s) {
   return c.used;
 }
 
-int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
-                 const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+// verify_block, and with `cache` set verify_block_cached: the expert weights
+// then come from the cache's device slots, after the missing ones are copied
+// in (one stream synchronization after the selection)
+static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                     const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
+                     acceptmoe_cache_report* report, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
   int rc = check_shape(s, true);
   if (rc) return rc;
   if (!in || !out) return fail(ACCEPTMOE_EINVAL, "inputs or outputs is NULL");
   const bool lin = (s->flags & ACCEPTMOE_F_LOGITS_IN) != 0;
   if (lin ? !in->logits_in : (!in->x || !in->w_router))
     return fail(ACCEPTMOE_EINVAL, lin ? "logits_in is NULL" : "x or w_router is NULL");
-  if (!in->x || !in->parent || !in->depth || !in->commit || !in->w13 || !in->w2 || !out->y || !ws)
+  if (!in->x || !in->parent || !in->depth || !in->commit || !out->y || !ws)
     return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  if (!cache && (!in->w13 || !in->w2)) return fail(ACCEPTMOE_EINVAL, "w13 or w2 is NULL");
+  if (cache) {
+    rc = check_cache(s, cache);
+    if (rc) return rc;
+  }
   const bool fp8 = s->w_dtype == ACCEPTMOE_FP8_E4M3FN;
   if (fp8 && (!in->s13 || !in->s2)) return fail(ACCEPTMOE_EINVAL, "FP8 weights need s13 and s2");
   const bool shared = in->w13_shared != nullptr;
@@ -466,7 +637,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.parent = in->parent;
   a.depth = in->depth;
   a.commit = in->commit;
-  a.resident = in->resident;
+  a.resident = cache ? cache->dev_resident : in->resident;
   a.logits_out = out->logits_out;
   a.eligible = eligible;
   a.topk_idx = topk_idx;
@@ -483,6 +654,10 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
   if (rc) return rc;
   timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
+  if (cache) {
+    rc = cache_fetch(s, cache, active, w.n_active, report, stream);
+    if (rc) return rc;
+  }
   amoe::GroupedArgs g;
   g.N = s->N;
   g.k = s->k;
@@ -492,8 +667,8 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.w_kind = w_kind(s->w_dtype);
   g.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
   g.x = in->x;
-  g.w13 = in->w13;
-  g.w2 = in->w2;
+  g.w13 = cache ? cache->dev_w13 : in->w13;
+  g.w2 = cache ? cache->dev_w2 : in->w2;
   g.s13 = in->s13;
   g.s2 = in->s2;
   g.offsets = w.offsets;
@@ -508,6 +683,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   // combine gathers without inv_pos (same values, same arithmetic)
   g.tok_rows = g.w_kind != 0;
   g.row_groups = 1;
+  g.w_slot = cache ? cache->dev_expert_slot : nullptr;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
   rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
@@ -538,6 +714,7 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.y_perm = w.sh_y;
     gs.h_perm = w.sh_h;
     gs.tok_rows = 0;
+    gs.w_slot = nullptr;
     gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
     if (rc) return rc;
@@ -548,6 +725,29 @@ int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
                   "verify_block/combine");
   timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);
   return rc;
+}
+
+int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                 const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_block(s, in, nullptr, out, nullptr, ws, ws_bytes, stream);
+}
+
+int verify_block_cached(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                        const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
+                        acceptmoe_cache_report* report, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!cache) return fail(ACCEPTMOE_EINVAL, "cache is NULL");
+  return run_block(s, in, cache, out, report, ws, ws_bytes, stream);
+}
+
+int acceptmoe_cache_plan(acceptmoe_cache_state* st, const int32_t* active, int32_t n_active,
+                         int32_t* fetch_expert, int32_t* fetch_slot, int32_t* n_fetch) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  if (n_active < 0 || n_active > st->E || (n_active > 0 && !active) || !fetch_expert ||
+      !fetch_slot || !n_fetch)
+    return fail(ACCEPTMOE_EINVAL, "acceptmoe_cache_plan: bad active list or output pointer");
+  return plan_fetches(st, active, n_active, fetch_expert, fetch_slot, n_fetch, nullptr);
 }
 
 }  // extern "C"

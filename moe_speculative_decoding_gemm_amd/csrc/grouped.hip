@@ -452,6 +452,7 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
     const int e = a.active[u];
     const int off = a.offsets[e];
     const int te = a.offsets[e + 1] - off;
+    const int ew = a.w_slot ? a.w_slot[e] : e;  // where expert e's weights sit
 
     const WTp* wrow[NT];
     int orow[NT];   // gate/up: intermediate index i; down: hidden index h
@@ -465,19 +466,19 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         const int irow = q * 8 + (r & 7);
         orow[nt] = irow;
         srow[nt] = (e * 2 + half) * (I >> 7) + (irow >> 7);
-        wrow[nt] = w13 + (static_cast<size_t>(e * 2 + half) * I + irow) * H + 8 * g;
+        wrow[nt] = w13 + (static_cast<size_t>(ew * 2 + half) * I + irow) * H + 8 * g;
       } else {
         const int hrow = q * 16 + r;
         orow[nt] = hrow;
         srow[nt] = e * (H >> 7) + (hrow >> 7);
-        wrow[nt] = w2 + (static_cast<size_t>(e) * H + hrow) * I + 8 * g;
+        wrow[nt] = w2 + (static_cast<size_t>(ew) * H + hrow) * I + 8 * g;
       }
     }
     const float* scales = GATEUP ? a.s13 : a.s2;
     const int nkb = K >> 7;
     // packed: this wave's fragments of the item, chunk-major (see pack_kernel)
     const WTp* pbase = static_cast<const WTp*>(GATEUP ? a.w13 : a.w2) +
-                       (static_cast<size_t>(e) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
+                       (static_cast<size_t>(ew) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
                        static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
 
     for (int mg = g0 * ROWS; mg < te; mg += R * ROWS) {

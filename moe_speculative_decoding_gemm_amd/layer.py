@@ -93,3 +93,15 @@ class VerifyLayer:
                       logits_in=logits_in)
         L.verify_block(self.shape, inputs, self.out, self.ws, stream=stream)
         return self.out
+
+    def run_cached(self, cache, x, parent, depth, commit,
+                   logits_in: Optional[torch.Tensor] = None, stream=None) -> dict:
+        """The block with the routed experts' weights from an ExpertCache
+        (the cache's resident mask drives residency-aware pruning).  Returns
+        the outputs; the call's cache report is in ``self.report``."""
+        inputs = dict(self.w)
+        inputs.update(x=x, parent=parent, depth=depth, commit=commit, resident=None,
+                      logits_in=logits_in, w13=None, w2=None)
+        self.report = L.verify_block_cached(self.shape, inputs, cache.desc, self.out, self.ws,
+                                            stream=stream)
+        return self.out
