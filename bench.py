@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--moesd-sweep", action="store_true",
                     help="instead of the headline run: natural-routing layer time T(B, gamma) for "
                          "B sequences x gamma-token chains, and eta(B, gamma) = T(B,1)/T(B,gamma)")
+    ap.add_argument("--offload", action="store_true",
+                    help="physical expert offload: a 48-slot expert cache per layer, natural "
+                         "routing vs AcceptMoE vs AcceptMoE + residency-aware pruning")
+    ap.add_argument("--offload-config", default="gptoss_120b")
+    ap.add_argument("--offload-blocks", type=int, default=24)
+    ap.add_argument("--offload-slots", type=int, default=48)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--flags", type=int, default=None, help="override shape flags (1 = natural)")
     ap.add_argument("--fixed-budget", type=int, default=None)
@@ -83,6 +89,9 @@ def main():
         return
     if args.moesd_sweep:
         moesd_sweep(args)
+        return
+    if args.offload:
+        offload_sweep(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -407,6 +416,109 @@ def moesd_sweep(args):
     print(json.dumps({"sweep": "moesd_target_efficiency", "workload": f"{base.name}: E={base.E} "
                       f"k={base.k} H={base.H} I={base.I}, {base.w} experts, natural routing, "
                       "B chains of gamma tokens", "points": points}), flush=True)
+
+
+def offload_sweep(args):
+    """[AcceptMoE news §02, §03]: physical expert offload with a per-layer cache
+    of 48 device expert slots (LRU), the other experts' packed weights in
+    pinned host memory.  The same seeded blocks run through
+    verify_block_cached under natural routing, AcceptMoE, and AcceptMoE with
+    residency-aware pruning, each from the same warm cache (the first block's
+    Zipf resident mask).  Per mode: time per block (selection, the one host
+    synchronization, host-to-device copies of the missing experts, experts,
+    combine), host-to-device expert bytes, the expert-cache hit rate, the share
+    of the block spent in the copies, and the copies' rate.  Next to them: the
+    same blocks with every expert in HBM (verify_block)."""
+    import torch
+    import moe_speculative_decoding_gemm_amd as M
+    import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIGS[args.offload_config]
+    DT = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3FN}
+    shape = M.make_shape(cfg.N, cfg.H, cfg.I, cfg.E, cfg.k, cfg.n_depth,
+                         act_dtype=DT[cfg.act], w_dtype=DT[cfg.w], min_set=cfg.min_set,
+                         fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute)
+    t0 = time.time()
+    blocks = [W.make_block(cfg, s) for s in range(args.offload_blocks)]
+    b0 = blocks[0]
+    ew = W.expert_weights(cfg, layer=0, device=dev)
+    layer = M.VerifyLayer(shape, dict(w_router=b0.w_router.to(dev),
+                                      b_router=None if b0.b_router is None else b0.b_router.to(dev),
+                                      w13=ew["w13"], w2=ew["w2"], s13=ew["s13"], s2=ew["s2"]),
+                          device=dev)
+    del ew
+    n_slots = args.offload_slots
+    cache = M.ExpertCache(layer.shape, n_slots, cfg.E - n_slots, layer.w["w13"], layer.w["w2"],
+                          device=dev)
+    warm = [int(e) for e in b0.resident.nonzero()[0]][:n_slots] if b0.resident is not None \
+        else list(range(n_slots))
+    dblocks = [dict(x=b.x.to(dev), parent=torch.from_numpy(b.parent).to(dev),
+                    depth=torch.from_numpy(b.depth).to(dev),
+                    commit=torch.from_numpy(b.commit).to(dev)) for b in blocks]
+    torch.cuda.synchronize()
+    log(f"offload setup {time.time() - t0:.1f}s: {cfg.name}, {cfg.E} experts of "
+        f"{cache.b13 + cache.b2} packed bytes, {n_slots} slots")
+    modes = {"natural": dict(flags=M.F_NATURAL, reroute_budget=0),
+             "acceptmoe": dict(flags=0, reroute_budget=0),
+             "acceptmoe_rap": dict(flags=0, reroute_budget=cfg.reroute)}
+    per_expert = cache.b13 + cache.b2
+    results = {}
+    for name, fields in modes.items():
+        lv = layer.variant(**fields)
+        d = dblocks[0]
+        cache.reset(warm)       # one untimed call (first-launch costs), then the real start
+        lv.run_cached(cache, d["x"], d["parent"], d["depth"], d["commit"])
+        cache.reset(warm)
+        ms, fetch_ms, us_res, U = [], [], [], []
+        for d in dblocks:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
+            f1.record()
+            M.acceptmoe_set_stage_timer(M.STAGE_FETCH, f0.cuda_event, f1.cuda_event)
+            e0.record()
+            lv.run_cached(cache, d["x"], d["parent"], d["depth"], d["commit"])
+            e1.record()
+            M.acceptmoe_set_stage_timer(M.STAGE_NONE, None, None)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+            fetch_ms.append(f0.elapsed_time(f1) if lv.report["n_fetched"] else 0.0)
+            U.append(lv.report["n_active"])
+        cnt = cache.counters()
+        # the same blocks with every expert in HBM (resident mask of the warm cache)
+        resident = torch.zeros(cfg.E, dtype=torch.uint8, device=dev)
+        resident[warm] = 1
+        for d in dblocks:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lv.run(d["x"], d["parent"], d["depth"], d["commit"], resident=resident)
+            e1.record()
+            torch.cuda.synchronize()
+            us_res.append(e0.elapsed_time(e1) * 1e3)
+        nb = len(dblocks)
+        tot_fetch = sum(fetch_ms)
+        results[name] = {
+            "ms_per_block": round(statistics.mean(ms), 3),
+            "U_mean": statistics.mean(U),
+            "h2d_GB_per_block": round(cnt["h2d_bytes"] / nb / 1e9, 4),
+            "experts_fetched_per_block": cnt["misses"] / nb,
+            "hit_rate": round(cnt["hits"] / max(1, cnt["hits"] + cnt["misses"]), 4),
+            "spills": cnt["spills"],
+            "fetch_share": round(tot_fetch / sum(ms), 4),
+            "h2d_GBps": round(cnt["h2d_bytes"] / (tot_fetch * 1e-3) / 1e9, 1) if tot_fetch else None,
+            "all_resident_us_per_block": round(statistics.mean(us_res), 1),
+        }
+        log(f"{name}: {results[name]}")
+    nat = results["natural"]
+    for name, r in results.items():
+        r["speedup_vs_natural"] = round(nat["ms_per_block"] / r["ms_per_block"], 3)
+        r["h2d_reduction_vs_natural"] = round(1.0 - r["h2d_GB_per_block"] / nat["h2d_GB_per_block"],
+                                              4) if nat["h2d_GB_per_block"] else None
+    print(json.dumps({"sweep": "expert_offload", "workload": f"{cfg.name}: E={cfg.E} k={cfg.k} "
+                      f"H={cfg.H} I={cfg.I} N={cfg.N}, {cfg.w} experts, {n_slots} device slots "
+                      f"(LRU), the rest in pinned host memory, {nb} seeded blocks in sequence",
+                      "expert_bytes": per_expert, "modes": results}), flush=True)
 
 
 def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):

@@ -93,8 +93,11 @@ struct GroupedArgs {
   // time.
   int row_groups;
   // bf16 / fp8: when set, expert e's weights are entry w_slot[e] of w13 / w2
-  // (an expert cache of device slots); FP8 scales stay indexed by e
+  // (an expert cache of n_wslots device slots; an entry outside them is
+  // clamped, so a bad table cannot send a load out of the buffers); FP8
+  // scales stay indexed by e
   const int32_t* w_slot;
+  int n_wslots;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);

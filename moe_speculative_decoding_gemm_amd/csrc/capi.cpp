@@ -338,6 +338,8 @@ int check_cache(const acceptmoe_shape* s, const acceptmoe_expert_cache* c) {
     return fail(ACCEPTMOE_ENOTSUP, "the expert cache holds packed BF16 or FP8 weights");
   int rc = check_state(c->state);
   if (rc) return rc;
+  if (c->state->n_slots + c->state->n_spill < 1)
+    return fail(ACCEPTMOE_EINVAL, "the cache has no device slots");
   if (c->state->E != s->E)
     return fail(ACCEPTMOE_EINVAL, "cache state E=%d != shape E=%d", c->state->E, s->E);
   if (!c->host_w13 || !c->host_w2 || !c->dev_w13 || !c->dev_w2 || !c->dev_expert_slot ||
@@ -535,6 +537,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   // one expert (the shared expert) takes every row: spread its row groups
   a.row_groups = E == 1 ? (N * k + 63) / 64 : 1;
   a.w_slot = nullptr;
+  a.n_wslots = 0;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -684,6 +687,7 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.tok_rows = g.w_kind != 0;
   g.row_groups = 1;
   g.w_slot = cache ? cache->dev_expert_slot : nullptr;
+  g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
   rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
@@ -715,6 +719,7 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.h_perm = w.sh_h;
     gs.tok_rows = 0;
     gs.w_slot = nullptr;
+    gs.n_wslots = 0;
     gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
     if (rc) return rc;

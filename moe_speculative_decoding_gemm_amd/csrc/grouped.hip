@@ -452,7 +452,8 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
     const int e = a.active[u];
     const int off = a.offsets[e];
     const int te = a.offsets[e + 1] - off;
-    const int ew = a.w_slot ? a.w_slot[e] : e;  // where expert e's weights sit
+    // where expert e's weights sit
+    const int ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
 
     const WTp* wrow[NT];
     int orow[NT];   // gate/up: intermediate index i; down: hidden index h
