@@ -333,7 +333,7 @@ int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop);
  *
  * verify_block_cached: verify_block with the routed experts' weights taken
  * from the cache.  The selection's resident mask is cache->dev_resident (so
- * ACCEPTMOE residency-aware pruning applies when reroute_budget > 0); the
+ * residency-aware pruning applies when reroute_budget > 0); the
  * active experts are copied back to the host and the stream is synchronized
  * once; the plan's missing experts are copied host -> device into their
  * slots with hipMemcpyAsync on `stream`, followed by dev_expert_slot and

@@ -24,6 +24,8 @@ Modules:
   residency-aware pruning, restricted top-k, gates), permute, grouped SwiGLU
   experts, combine.
 * :mod:`oracle.fp8` -- OCP E4M3FN decoding for the fp8 expert weights.
+* :mod:`oracle.cache` -- the expert cache under physical expert offload
+  (least-recently-used slots; a reading, the pages give no policy).
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 page examples, closed forms, library routines or brute force, except where a
