@@ -60,6 +60,9 @@ SMALL = [
     ("qwen3_30b", dict(E=40, k=8, H=192, I=2112, N=64)),
     ("qwen3_30b", dict(E=40, k=8, H=2112, I=192, N=64)),
     ("dsv31", dict(E=24, k=8, H=256, I=2304, N=64, n_chains=8, chain_len=8)),
+    # natural routing over 40 experts: 3-tile items (48 weight rows) in both
+    # projections, with a shorter last item per expert (32 and 16 tiles)
+    ("qwen3_30b", dict(E=40, k=8, H=256, I=256, N=64, flags=1)),
 ]
 
 
