@@ -464,8 +464,12 @@ def offload_sweep(args):
              "acceptmoe_rap": dict(flags=0, reroute_budget=cfg.reroute)}
     per_expert = cache.b13 + cache.b2
     results = {}
-    for name, fields in modes.items():
-        lv = layer.variant(**fields)
+    runs = [(name, fields, ov) for ov in (False, True) for name, fields in modes.items()]
+    for name, fields, ov in runs:
+        cache.set_overlap(ov)
+        if ov:
+            name = name + "_overlap"
+        lv = layer.variant(**{k: v for k, v in fields.items()})
         d = dblocks[0]
         cache.reset(warm)       # one untimed call (first-launch costs), then the real start
         lv.run_cached(cache, d["x"], d["parent"], d["depth"], d["commit"])
@@ -515,6 +519,8 @@ def offload_sweep(args):
         r["speedup_vs_natural"] = round(nat["ms_per_block"] / r["ms_per_block"], 3)
         r["h2d_reduction_vs_natural"] = round(1.0 - r["h2d_GB_per_block"] / nat["h2d_GB_per_block"],
                                               4) if nat["h2d_GB_per_block"] else None
+        if name.endswith("_overlap"):
+            r["speedup_vs_serial"] = round(results[name[:-8]]["ms_per_block"] / r["ms_per_block"], 3)
     print(json.dumps({"sweep": "expert_offload", "workload": f"{cfg.name}: E={cfg.E} k={cfg.k} "
                       f"H={cfg.H} I={cfg.I} N={cfg.N}, {cfg.w} experts, {n_slots} device slots "
                       f"(LRU), the rest in pinned host memory, {nb} seeded blocks in sequence",

@@ -344,6 +344,14 @@ int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop);
  * capturable in a HIP graph (it synchronizes).  The state's tables must not
  * change while the call's copies are pending on the stream.  report (host,
  * may be NULL) receives this call's counts.
+ *
+ * Overlap: with copy_stream, copy_done and dev_lists set (a stream of the
+ * default priority, an event, 2E+2 device ints, all the caller's), the
+ * missing experts are copied on copy_stream while the experts that hit run on
+ * `stream`; `stream` then waits for copy_done and runs the fetched experts
+ * ([MoE-SD blog, CPU offload section] counts the overlap of transfers
+ * with compute among the measures of an offload system).  Results are identical: every
+ * expert's rows are computed by the same kernels, only in two launches.
  * ------------------------------------------------------------------------- */
 typedef struct acceptmoe_cache_state {
   int32_t E;              /* routed experts                                      */
@@ -366,6 +374,9 @@ typedef struct acceptmoe_expert_cache {
   void* dev_w2;                   /* device, packed w2 of n_slots + n_spill slots  */
   int32_t* dev_expert_slot;       /* device [E]                                    */
   uint8_t* dev_resident;          /* device [E]                                    */
+  hipStream_t copy_stream;        /* or NULL: the copies run on the call's stream  */
+  hipEvent_t copy_done;           /* with copy_stream                              */
+  int32_t* dev_lists;             /* device [2E+2], with copy_stream               */
 } acceptmoe_expert_cache;
 
 typedef struct acceptmoe_cache_report {  /* one verify_block_cached call      */

@@ -66,7 +66,9 @@ class CacheState(C.Structure):
 class ExpertCacheDesc(C.Structure):
     _fields_ = [("state", C.c_void_p), ("host_w13", C.c_void_p), ("host_w2", C.c_void_p),
                 ("dev_w13", C.c_void_p), ("dev_w2", C.c_void_p),
-                ("dev_expert_slot", C.c_void_p), ("dev_resident", C.c_void_p)]
+                ("dev_expert_slot", C.c_void_p), ("dev_resident", C.c_void_p),
+                ("copy_stream", C.c_void_p), ("copy_done", C.c_void_p),
+                ("dev_lists", C.c_void_p)]
 
 
 class CacheReport(C.Structure):

@@ -29,7 +29,7 @@ class ExpertCache:
 
     def __init__(self, shape: L.Shape, n_slots: int, n_spill: int,
                  w13_packed: Optional[torch.Tensor] = None,
-                 w2_packed: Optional[torch.Tensor] = None, device=None):
+                 w2_packed: Optional[torch.Tensor] = None, device=None, overlap: bool = False):
         E = shape.E
         self.E, self.n_slots, self.n_spill = E, n_slots, n_spill
         pin = device is not None
@@ -64,7 +64,24 @@ class ExpertCache:
         self.desc = L.ExpertCacheDesc(
             C.addressof(self.state), self.host_w13.data_ptr(), self.host_w2.data_ptr(),
             self.dev_w13.data_ptr(), self.dev_w2.data_ptr(), self.dev_expert_slot.data_ptr(),
-            self.dev_resident.data_ptr())
+            self.dev_resident.data_ptr(), None, None, None)
+        self.set_overlap(overlap)
+
+    def set_overlap(self, on: bool):
+        """Copy the missing experts on a stream of their own (default
+        priority) while the hit experts run, or on the call's stream."""
+        if on and getattr(self, "copy_stream", None) is None:
+            self.copy_stream = torch.cuda.Stream(device=self.device)
+            self.copy_done = torch.cuda.Event()
+            self.copy_done.record(self.copy_stream)  # creates the event handle
+            self.dev_lists = torch.zeros(2 * self.E + 2, dtype=torch.int32, device=self.device)
+            torch.cuda.synchronize(self.device)
+        if on:
+            self.desc.copy_stream = self.copy_stream.cuda_stream
+            self.desc.copy_done = self.copy_done.cuda_event
+            self.desc.dev_lists = self.dev_lists.data_ptr()
+        else:
+            self.desc.copy_stream = self.desc.copy_done = self.desc.dev_lists = None
 
     def reset(self, experts: Iterable[int] = ()):
         """Empty the cache, then place `experts` in slots 0, 1, ... (a warm

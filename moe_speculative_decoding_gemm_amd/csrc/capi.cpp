@@ -352,7 +352,8 @@ int check_cache(const acceptmoe_shape* s, const acceptmoe_expert_cache* c) {
 // synchronization), plan, copy the missing experts' packed weights from
 // host memory into their slots, then the slot table and resident mask.
 int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const int32_t* active,
-                const int32_t* n_active, acceptmoe_cache_report* report, hipStream_t stream) {
+                const int32_t* n_active, acceptmoe_cache_report* report, hipStream_t stream,
+                bool* overlap) {
   acceptmoe_cache_state* st = c->state;
   int32_t host_n = 0;
   int32_t host_active[256];
@@ -376,18 +377,42 @@ int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const
   const char* h2 = static_cast<const char*>(c->host_w2);
   char* d13 = static_cast<char*>(c->dev_w13);
   char* d2 = static_cast<char*>(c->dev_w2);
-  timer_mark(ACCEPTMOE_STAGE_FETCH, true, stream);
-  for (int f = 0; f < nf && e == hipSuccess; ++f) {
-    e = hipMemcpyAsync(d13 + b13 * fs[f], h13 + b13 * fe[f], b13, hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(d2 + b2 * fs[f], h2 + b2 * fe[f], b2, hipMemcpyHostToDevice, stream);
-  }
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(c->dev_expert_slot, st->expert_slot, sizeof(int32_t) * s->E,
-                       hipMemcpyHostToDevice, stream);
+  // the slot table and resident mask first, on the launch stream: every
+  // expert kernel of this block reads the table
+  e = hipMemcpyAsync(c->dev_expert_slot, st->expert_slot, sizeof(int32_t) * s->E,
+                     hipMemcpyHostToDevice, stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(c->dev_resident, st->resident, s->E, hipMemcpyHostToDevice, stream);
-  timer_mark(ACCEPTMOE_STAGE_FETCH, false, stream);
+  // with a copy stream, the hit and the missing experts run as two passes:
+  // lists [hits (E)] [n_hits] [misses (E)] [n_misses]
+  *overlap = c->copy_stream != nullptr && c->copy_done != nullptr && c->dev_lists != nullptr &&
+             nf > 0;
+  hipStream_t cs = *overlap ? c->copy_stream : stream;
+  if (*overlap && e == hipSuccess) {
+    const int E = s->E;
+    int32_t lists[2 * 256 + 2];
+    uint8_t miss[256];
+    std::memset(miss, 0, sizeof(miss));
+    for (int f = 0; f < nf; ++f) miss[fe[f]] = 1;
+    int nh = 0;
+    for (int u = 0; u < host_n; ++u)
+      if (!miss[host_active[u]]) lists[nh++] = host_active[u];
+    for (int u = nh; u < E; ++u) lists[u] = 0;
+    lists[E] = nh;
+    for (int f = 0; f < nf; ++f) lists[E + 1 + f] = fe[f];
+    for (int f = nf; f < E; ++f) lists[E + 1 + f] = 0;
+    lists[2 * E + 1] = nf;
+    e = hipMemcpyAsync(c->dev_lists, lists, sizeof(int32_t) * (2 * E + 2), hipMemcpyHostToDevice,
+                       stream);
+  }
+  timer_mark(ACCEPTMOE_STAGE_FETCH, true, cs);
+  for (int f = 0; f < nf && e == hipSuccess; ++f) {
+    e = hipMemcpyAsync(d13 + b13 * fs[f], h13 + b13 * fe[f], b13, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d2 + b2 * fs[f], h2 + b2 * fe[f], b2, hipMemcpyHostToDevice, cs);
+  }
+  timer_mark(ACCEPTMOE_STAGE_FETCH, false, cs);
+  if (*overlap && e == hipSuccess) e = hipEventRecord(c->copy_done, cs);
   rc = hip_status(e, "verify_block_cached/fetch");
   if (rc) return rc;
   rep.h2d_bytes = static_cast<int64_t>(nf) * static_cast<int64_t>(b13 + b2);
@@ -657,8 +682,9 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
   if (rc) return rc;
   timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
+  bool overlap = false;
   if (cache) {
-    rc = cache_fetch(s, cache, active, w.n_active, report, stream);
+    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
     if (rc) return rc;
   }
   amoe::GroupedArgs g;
@@ -689,14 +715,29 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.w_slot = cache ? cache->dev_expert_slot : nullptr;
   g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
-  timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
-  rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
-  if (rc) return rc;
-  timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
-  timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
-  rc = hip_status(amoe::launch_grouped(g, stream, 2), "verify_block/experts down");
-  if (rc) return rc;
-  timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
+  if (overlap) {
+    // the hit experts while the missing ones are copied in, then those
+    const int32_t* lists = cache->dev_lists;
+    g.active = lists;
+    g.n_active = lists + s->E;
+    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");
+    if (rc) return rc;
+    rc = hip_status(hipStreamWaitEvent(stream, cache->copy_done, 0), "verify_block_cached/wait");
+    if (rc) return rc;
+    g.active = lists + s->E + 1;
+    g.n_active = lists + 2 * s->E + 1;
+    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched experts");
+    if (rc) return rc;
+  } else {
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
+    rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
+    timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
+    rc = hip_status(amoe::launch_grouped(g, stream, 2), "verify_block/experts down");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
+  }
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, false, stream);
   timer_mark(ACCEPTMOE_STAGE_COMBINE, true, stream);
   if (shared) {

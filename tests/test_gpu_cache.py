@@ -1,4 +1,5 @@
-"""GPU tests of physical expert offload (verify_block_cached).
+"""GPU tests of physical expert offload (verify_block_cached), with the
+copies on the call's stream and on a copy stream overlapping the hit experts.
 
 A sequence of seeded blocks runs through verify_block_cached on an expert
 cache of a few device slots.  Each block must give bit-identical outputs to
@@ -36,8 +37,9 @@ def warm_set(cfg, b, slots):
     return list(range(slots))
 
 
+@pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
 @pytest.mark.parametrize("name,over,slots,spill", CASES)
-def test_cached_block_matches_resident_block(lib, name, over, slots, spill):
+def test_cached_block_matches_resident_block(lib, name, over, slots, spill, overlap):
     cfg = W.CONFIGS[name].with_(**over)
     w = make_weights(cfg, device="cuda", gen_device="cpu")
     b0 = W.make_block(cfg, 0)
@@ -46,14 +48,14 @@ def test_cached_block_matches_resident_block(lib, name, over, slots, spill):
                                                      b_router=d0["b_router"], **w), pack=True)
     plain = layer.variant()
     cache = lib.ExpertCache(layer.shape, slots, spill, layer.w["w13"], layer.w["w2"],
-                            device="cuda")
+                            device="cuda", overlap=overlap)
     warm = warm_set(cfg, b0, slots)
     cache.reset(warm)
     model = LRUExpertCache(slots, spill, warm)
     per_expert = cache.b13 + cache.b2
     total = 0
     for seed in range(6):
-        say(f"cache {name} {over} slots={slots} spill={spill} seed {seed}")
+        say(f"cache {name} {over} slots={slots} spill={spill} overlap={overlap} seed {seed}")
         b = W.make_block(cfg, seed)
         d = upload_block(b)
         res_before = cache.resident.clone().cuda()
