@@ -155,17 +155,18 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 // logits_in, fp64 softmax statistics, natural top-k (written in slot order),
 // demand terms into sm.c[slot], anchor / natural-use flags, error bits.
 // d, p, dp, cf: depth, parent, parent's depth and commit[depth] of node i.
+template <int Q>
 __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot, NodeSmem& sm,
                                            int d, int p, int dp, float cf, const float* bias) {
   const int lane = lane_id();
   const int E = a.E, k = a.k;
   const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
-  float l[4];
-  bool valid[4];
+  float l[Q];
+  bool valid[Q];
   bool nonfinite = false;
   if (logits_in) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       valid[q] = e < E;
       l[q] = valid[q] ? a.logits_in[static_cast<size_t>(i) * E + e] : 0.f;
@@ -173,9 +174,9 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
   } else {
     // K-slice partial sums: every load issued first, then summed in slice order
     const size_t stride = static_cast<size_t>(a.N) * E;
-    float pv[4][kMaxKSplit];
+    float pv[Q][kMaxKSplit];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       valid[q] = e < E;
       const float* pp = a.part + static_cast<size_t>(i) * E + e;
@@ -184,7 +185,7 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
         if (valid[q] && s < a.ksplit) pv[q][s] = load_dev(pp + s * stride);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       float sum = 0.f;
 #pragma unroll
       for (int s = 0; s < kMaxKSplit; ++s)
@@ -193,7 +194,7 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < Q; ++q) {
     if (valid[q]) {
       const int e = lane + kWave * q;
       a.logits[static_cast<size_t>(i) * E + e] = l[q];
@@ -203,35 +204,43 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < Q; ++q)
     if (valid[q]) m = fmaxf(m, l[q]);
   m = wave_max_f32(m);
   double zs = 0.0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < Q; ++q)
     if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
   const double z = wave_sum_f64(zs);
 
   // natural top-k: k rounds of a wave max over 32-bit order keys; among equal
   // keys the lowest expert index (slot q, then lane) wins
-  uint32_t key[4];
+  uint32_t key[Q];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) key[q] = valid[q] ? order_key(l[q]) : 0u;
+  for (int q = 0; q < Q; ++q) key[q] = valid[q] ? order_key(l[q]) : 0u;
   uint32_t in_nat = 0;  // bit q: slot q is in the natural top-k
   int my_e = 0;         // lane j: expert of rank j
   uint32_t my_o = 0;    //         and its key
   for (int j = 0; j < k; ++j) {
-    uint32_t b = key[0] > key[1] ? key[0] : key[1];
-    const uint32_t b2 = key[2] > key[3] ? key[2] : key[3];
-    b = wave_max_u32(b > b2 ? b : b2);
-    const uint64_t m0 = __ballot(key[0] == b), m1 = __ballot(key[1] == b);
-    const uint64_t m2 = __ballot(key[2] == b), m3 = __ballot(key[3] == b);
-    const int qw = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : 3));
-    const uint64_t mw = m0 ? m0 : (m1 ? m1 : (m2 ? m2 : m3));
+    uint32_t b = key[0];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) b = key[q] > b ? key[q] : b;
+    b = wave_max_u32(b);
+    // the lowest slot q holding the maximum, then its lowest lane
+    int qw = Q - 1;
+    uint64_t mw = __ballot(key[Q - 1] == b);
+#pragma unroll
+    for (int q = Q - 2; q >= 0; --q) {
+      const uint64_t mq = __ballot(key[q] == b);
+      if (mq) {
+        qw = q;
+        mw = mq;
+      }
+    }
     const int lw = static_cast<int>(__builtin_ctzll(mw));
     if (lane == lw) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < Q; ++q)
         if (q == qw) {
           key[q] = 0u;
           in_nat |= 1u << q;
@@ -255,7 +264,7 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
   const double c = (a.flags & kFlagUnitCommit) ? 1.0 : static_cast<double>(cf);
   const int fl = (p == -1 && !(a.flags & kFlagNoAnchor)) ? 3 : 2;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const bool nat_q = (in_nat & (1u << q)) != 0;
     const int e = lane + kWave * q;
     if (full ? valid[q] : nat_q)
@@ -336,6 +345,9 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     sm.ncand = 0;
   }
   __syncthreads();
+  // error words and the commit table, loaded together with the demand rows
+  const int err0 = t < nwg ? a.e_part[t] : 0;
+  const float com0 = t < a.n_depth ? a.commit[t] : 0.f;
   // demand per expert: its row of group partials summed in group order
   // (16-byte loads: two partials, sixteen flag bytes)
   int f = 0;
@@ -367,11 +379,13 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     sm.d[t] = dsum;
     sm.anchor[t] = f & 1;
   }
-  for (int w = t; w < nwg; w += kTail) {
+  if (err0) atomicOr(&sm.err, err0);
+  for (int w = t + kTail; w < nwg; w += kTail) {
     const int e = a.e_part[w];
     if (e) atomicOr(&sm.err, e);
   }
-  for (int dd = t; dd < a.n_depth; dd += kTail) {
+  if (t < a.n_depth && (!(com0 >= 0.f) || isinf(com0))) atomicOr(&sm.err, kErrCommit);
+  for (int dd = t + kTail; dd < a.n_depth; dd += kTail) {
     const float c = a.commit[dd];
     if (!(c >= 0.f) || isinf(c)) atomicOr(&sm.err, kErrCommit);
   }
@@ -667,7 +681,8 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
 }
 
 // ------------------------------------------------------------- kernel ----
-template <typename AT>
+// Q: 64-expert slots per lane, ceil(E / 64)
+template <typename AT, int Q>
 __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   __shared__ NodeSmem sm;
   const int t = threadIdx.x, wave = t >> 6, lane = lane_id();
@@ -687,7 +702,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.b_router) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bias[q] = a.b_router[min(lane + kWave * q, E - 1)];
+    for (int q = 0; q < Q; ++q) bias[q] = a.b_router[min(lane + kWave * q, E - 1)];
   }
   float cf;
   int dp;
@@ -716,7 +731,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   }
   if (t == 0) sm.err = 0;
   __syncthreads();
-  if (has_node) node_phase(a, node, wave, sm, d, p, dp, cf, bias);
+  if (has_node) node_phase<Q>(a, node, wave, sm, d, p, dp, cf, bias);
   __syncthreads();
   const int ds = dpart_stride(N), fs = fpart_stride(N);
   for (int x = t; x < E; x += 256) {
@@ -865,10 +880,26 @@ size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N)) *
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const bool lin = (a.flags & kFlagLogitsIn) != 0;
   const dim3 grid(node_groups(a.N), lin ? 1 : a.ksplit, 1);
-  if (a.act_bf16)
-    front_kernel<uint16_t><<<grid, 256, 0, stream>>>(a);
-  else
-    front_kernel<float><<<grid, 256, 0, stream>>>(a);
+  const int q = (a.E + kWave - 1) / kWave;
+  if (a.act_bf16) {
+    if (q == 1)
+      front_kernel<uint16_t, 1><<<grid, 256, 0, stream>>>(a);
+    else if (q == 2)
+      front_kernel<uint16_t, 2><<<grid, 256, 0, stream>>>(a);
+    else if (q == 3)
+      front_kernel<uint16_t, 3><<<grid, 256, 0, stream>>>(a);
+    else
+      front_kernel<uint16_t, 4><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (q == 1)
+      front_kernel<float, 1><<<grid, 256, 0, stream>>>(a);
+    else if (q == 2)
+      front_kernel<float, 2><<<grid, 256, 0, stream>>>(a);
+    else if (q == 3)
+      front_kernel<float, 3><<<grid, 256, 0, stream>>>(a);
+    else
+      front_kernel<float, 4><<<grid, 256, 0, stream>>>(a);
+  }
   tail_kernel<<<1, kTail, 0, stream>>>(a);
   if (a.N > kFusedMaxN) restricted_kernel<<<node_groups(a.N), 256, 0, stream>>>(a);
   return hipGetLastError();
