@@ -208,9 +208,12 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
     if (valid[q]) m = fmaxf(m, l[q]);
   m = wave_max_f32(m);
   double zs = 0.0;
+  double ex[Q];  // exp(l - m), kept for the demand terms
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
-    if (valid[q]) zs += exp(static_cast<double>(l[q]) - static_cast<double>(m));
+  for (int q = 0; q < Q; ++q) {
+    ex[q] = valid[q] ? exp(static_cast<double>(l[q]) - static_cast<double>(m)) : 0.0;
+    if (valid[q]) zs += ex[q];
+  }
   const double z = wave_sum_f64(zs);
 
   // natural top-k: k rounds of a wave max over 32-bit order keys; among equal
@@ -268,7 +271,7 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
     const bool nat_q = (in_nat & (1u << q)) != 0;
     const int e = lane + kWave * q;
     if (full ? valid[q] : nat_q)
-      sm.c[slot][e] = c * (exp(static_cast<double>(l[q]) - static_cast<double>(m)) / z);
+      sm.c[slot][e] = c * (ex[q] / z);
     if (nat_q) atomicOr(&sm.flags[e], fl);
   }
   const bool any_nf = __ballot(nonfinite) != 0ull;
