@@ -48,6 +48,8 @@ struct SelectArgs {
   int32_t* inv_pos;
   int32_t* active;
   int32_t* n_active;
+  int32_t* max_rows;  // or null: the most rows routed to one expert
+  int32_t* groups;    // or null: the active experts' 64-row groups (see permute_block)
 };
 
 // router product, per-node softmax / natural top-k / demand terms, set
@@ -98,6 +100,12 @@ struct GroupedArgs {
   // scales stay indexed by e
   const int32_t* w_slot;
   int n_wslots;
+  // when both are set and some expert has more than 64 routed rows: the
+  // work units are (64-row group, item) pairs from the groups table, so an
+  // expert with many rows spreads its row groups over as many units, which
+  // read the item's weights at about the same time
+  const int32_t* max_rows;
+  const int32_t* groups;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);

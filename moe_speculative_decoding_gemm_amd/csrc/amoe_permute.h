@@ -59,7 +59,9 @@ struct PermuteSmem {
   int apos[kMaxE];
   int run[kMaxE];
   int w[NTHR / kWave][kMaxE];
-  int nact;
+  int ng[kMaxE];  // 64-row groups of each expert
+  int gs[kMaxE];  // their exclusive scan
+  int nact, ngrp;
 };
 
 // Requires blockDim.x == NTHR (256 or 1024).  topk_idx may point to global
@@ -71,7 +73,8 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
                                               int32_t* sorted_assign, int32_t* inv_pos,
                                               int32_t* active, int32_t* n_active,
                                               const uint8_t* resident, StatsDev* stats,
-                                              PermuteSmem<NTHR>& sm) {
+                                              PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
+                                              int32_t* groups = nullptr) {
   constexpr int NW = NTHR / kWave;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
@@ -83,14 +86,29 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   __syncthreads();
   for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
   __syncthreads();
-  if (t < E) sm.flag[t] = sm.cnt[t] > 0 ? 1 : 0;
+  if (t < E) {
+    sm.flag[t] = sm.cnt[t] > 0 ? 1 : 0;
+    sm.ng[t] = (sm.cnt[t] + 63) >> 6;
+  }
   __syncthreads();
   if (wave == 0) {
     wave_exclusive_scan_256(sm.cnt, sm.off, E);
     const int na = wave_exclusive_scan_256(sm.flag, sm.apos, E);
     if (lane == 0) sm.nact = na;
+  } else if (wave == 1 && groups) {
+    const int ng = wave_exclusive_scan_256(sm.ng, sm.gs, E);
+    if (lane == 0) sm.ngrp = ng;
   }
   __syncthreads();
+  // the 64-row groups of the active experts in active order, as
+  // (active index << 16 | group): groups[0] = count, groups[1 + g] = entry g
+  if (groups) {
+    if (t < E) {
+      const int n = sm.ng[t], base = sm.gs[t], u = sm.apos[t];
+      for (int j = 0; j < n; ++j) groups[1 + base + j] = (u << 16) | j;
+    }
+    if (t == 0) groups[0] = sm.ngrp;
+  }
   if (t < E) {
     counts[t] = sm.cnt[t];
     offsets[t] = sm.off[t];
@@ -99,6 +117,12 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   if (t == 0) {
     offsets[E] = total;
     n_active[0] = sm.nact;
+  }
+  if (max_rows && t >= kWave && t < 2 * kWave) {  // second wave: the most rows of any expert
+    int mr = 0;
+    for (int e = t - kWave; e < E; e += kWave) mr = max(mr, sm.cnt[e]);
+    mr = static_cast<int>(wave_max_u32(static_cast<uint32_t>(mr)));
+    if (t == kWave) max_rows[0] = mr;
   }
   if (stats && t < kWave) {
     int nr = 0;

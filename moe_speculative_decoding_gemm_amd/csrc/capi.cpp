@@ -154,6 +154,7 @@ struct VerifyWs {
   int32_t* inv_pos;
   int32_t* active;
   int32_t* n_active;
+  int32_t* groups;
   acceptmoe_stats* stats;
   void* h_perm;
   float* y_perm;
@@ -177,7 +178,9 @@ VerifyWs carve_verify(Carver& c, const acceptmoe_shape* s, bool shared) {
   w.sorted_assign = c.take<int32_t>(NK);
   w.inv_pos = c.take<int32_t>(NK);
   w.active = c.take<int32_t>(s->E);
-  w.n_active = c.take<int32_t>(1);
+  w.n_active = c.take<int32_t>(2);  // [1]: the most rows routed to one expert
+  // 64-row groups of the active experts: at most N*k/64 + E, plus the count
+  w.groups = c.take<int32_t>(2 + NK / 64 + s->E);
   w.stats = c.take<acceptmoe_stats>(1);
   w.h_perm = c.take<char>(NK * s->I * hidden_elem_bytes(s->w_dtype));
   w.y_perm = c.take<float>(NK * s->H);
@@ -563,6 +566,8 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.row_groups = E == 1 ? (N * k + 63) / 64 : 1;
   a.w_slot = nullptr;
   a.n_wslots = 0;
+  a.max_rows = nullptr;
+  a.groups = nullptr;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -678,6 +683,8 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.inv_pos = w.inv_pos;
   a.active = active;
   a.n_active = w.n_active;
+  a.max_rows = w.n_active + 1;
+  a.groups = w.groups;
   timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
   rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
   if (rc) return rc;
@@ -712,6 +719,8 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   // combine gathers without inv_pos (same values, same arithmetic)
   g.tok_rows = g.w_kind != 0;
   g.row_groups = 1;
+  g.max_rows = w.n_active + 1;
+  g.groups = w.groups;
   g.w_slot = cache ? cache->dev_expert_slot : nullptr;
   g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
@@ -760,6 +769,8 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.h_perm = w.sh_h;
     gs.tok_rows = 0;
     gs.w_slot = nullptr;
+    gs.max_rows = nullptr;
+    gs.groups = nullptr;
     gs.n_wslots = 0;
     gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");

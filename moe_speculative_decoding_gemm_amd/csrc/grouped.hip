@@ -445,10 +445,28 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
   const int src_ld = GATEUP ? H : I;
 
   const int R = a.row_groups > 1 ? a.row_groups : 1;
-  for (int unit = blockIdx.x; unit < n_items * R; unit += gridDim.x) {
-    const int item = unit % n_items, g0 = unit / n_items;
-    const int u = item / tiles;
-    const int tile = item - u * tiles;
+  // Units: (item, row groups g0, g0 + R, ...), or, once some expert has more
+  // than 64 routed rows, (64-row group, tile) pairs from the groups table
+  // (group-major, so the groups of one tile are `tiles` units apart and read
+  // its weights at about the same time).
+  const bool by_group = a.groups != nullptr && a.max_rows != nullptr && *a.max_rows > ROWS;
+  const int n_units = by_group ? a.groups[0] * tiles : n_items * R;
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    int u, tile, g0, rstep;
+    if (by_group) {
+      const int gi = unit / tiles;
+      tile = unit - gi * tiles;
+      const int gv = a.groups[1 + gi];
+      u = gv >> 16;
+      g0 = gv & 0xffff;
+      rstep = 1 << 16;  // this group only
+    } else {
+      const int item = unit % n_items;
+      g0 = unit / n_items;
+      u = item / tiles;
+      tile = item - u * tiles;
+      rstep = R;
+    }
     const int e = a.active[u];
     const int off = a.offsets[e];
     const int te = a.offsets[e + 1] - off;
@@ -482,7 +500,7 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
                        (static_cast<size_t>(ew) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
                        static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
 
-    for (int mg = g0 * ROWS; mg < te; mg += R * ROWS) {
+    for (int mg = g0 * ROWS; mg < te; mg += rstep * ROWS) {
       // One group of routed rows mg.. with MTV 16-row M tiles: only as many
       // activation rows are staged (and MFMA tiles computed) as the group
       // has, rounded up to 16, 32 or 64 -- rows past the routed ones would

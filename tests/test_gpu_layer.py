@@ -63,6 +63,10 @@ SMALL = [
     # natural routing over 40 experts: 3-tile items (48 weight rows) in both
     # projections, with a shorter last item per expert (32 and 16 tiles)
     ("qwen3_30b", dict(E=40, k=8, H=256, I=256, N=64, flags=1)),
+    # more than 64 rows per expert (up to ~200): each item's row groups run as
+    # separate units next to each other
+    ("qwen3_30b", dict(E=12, k=4, H=256, I=320, N=300)),
+    ("dsv31", dict(E=10, k=3, H=256, I=256, N=200, n_chains=25, chain_len=8)),
 ]
 
 
