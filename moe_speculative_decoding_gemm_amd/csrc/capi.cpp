@@ -725,8 +725,10 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   if (overlap) {
-    // the hit experts while the missing ones are copied in, then those
+    // the hit experts while the missing ones are copied in, then those (the
+    // row-group table indexes the full active list: not used for the two lists)
     const int32_t* lists = cache->dev_lists;
+    g.groups = nullptr;
     g.active = lists;
     g.n_active = lists + s->E;
     rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");

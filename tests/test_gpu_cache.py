@@ -28,6 +28,8 @@ CASES = [
     ("qwen3_30b", dict(E=24, k=4, H=320, I=192, N=37, flags=1), 4, 24),
     # fp8 weights with block scales and the shared expert
     ("dsv31", dict(E=20, k=3, H=384, I=256, N=40, n_chains=5, chain_len=8), 8, 20),
+    # experts with more than 64 rows (row-group work units)
+    ("qwen3_30b", dict(E=12, k=4, H=256, I=320, N=300), 4, 12),
 ]
 
 
