@@ -153,9 +153,10 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     if (valid && rank == 0) sm.w[wave][e] = __popcll(peers);
     __syncthreads();
     if (t < E) {
+      // only the waves that hold assignments in this round take part
+      const int nw = min(NW, (total - base + kWave - 1) / kWave);
       int run = sm.run[t];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
+      for (int w = 0; w < nw; ++w) {
         const int c = sm.w[w][t];
         sm.w[w][t] = run;
         run += c;

@@ -299,6 +299,8 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
 // over the kTail threads: thread (e, part) counts over one part of the keys
 // and the parts are added in LDS.  Call with the whole work-group; returns
 // the rank in threads t < E with take[t] set.
+// The caller must pass a work-group barrier before it writes key or scratch
+// again.
 __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E, bool desc,
                                           const int* take) {
   const int t = threadIdx.x;
@@ -327,7 +329,8 @@ __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E
   int rank = 0;
   if (t < E)
     for (int pp = 0; pp < tpe; ++pp) rank += scratch[pp * EP + t];
-  __syncthreads();
+  // no barrier here: both callers pass a barrier before scratch or key is
+  // written again
   return rank;
 }
 
