@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--moesd-sweep", action="store_true",
                     help="instead of the headline run: natural-routing layer time T(B, gamma) for "
                          "B sequences x gamma-token chains, and eta(B, gamma) = T(B,1)/T(B,gamma)")
+    ap.add_argument("--budget-sweep", action="store_true",
+                    help="fixed expert budget B = 8, 16, .., 128: us per block against active "
+                         "experts U, with a least-squares line")
     ap.add_argument("--offload", action="store_true",
                     help="physical expert offload: a 48-slot expert cache per layer, natural "
                          "routing vs AcceptMoE vs AcceptMoE + residency-aware pruning")
@@ -69,6 +72,28 @@ def parse():
                     help="only run a plain 256 MiB device copy 5 times (for scaling HBM "
                          "byte counters: FETCH_SIZE / WRITE_SIZE of a known-size copy)")
     return ap.parse_args()
+
+
+def measured_copy_gbps(torch) -> float:
+    """Read + write bandwidth of a plain 4 GiB device-to-device copy (the
+    second denominator next to the published 8 TB/s)."""
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def copy_calibration():
@@ -173,6 +198,9 @@ def main():
         stats.append(st)
         y_eager.append(out["y"].clone())
     U = [st["n_active"] for st in stats]
+    if args.budget_sweep:
+        budget_sweep(M, torch, cfg, layers, dblocks, slots, S, args.variant_steps)
+        return
     ebytes = cfg.expert_bytes() + cfg.scale_bytes()
     shared_bytes = ebytes if cfg.shared else 0
     uniq_bytes = [u * ebytes for u in U]
@@ -229,6 +257,25 @@ def main():
     uniq_gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log(f"timed {args.steps} steps: {us_block:.2f} us/block, unique-expert {uniq_gbps:.0f} GB/s "
         f"(wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
+
+    # per-block latency spread: events around each replay (each interval also
+    # holds the dispatch latency in front of the block's first kernel)
+    n_lat = min(args.steps, 200)
+    lat_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_lat)]
+    for i in range(n_lat):
+        lat_ev[i][0].record()
+        step(i)
+        lat_ev[i][1].record()
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) * 1e3 for a, b in lat_ev)
+
+    def pct(q):
+        return round(lat[min(len(lat) - 1, int(q * len(lat)))], 2)
+    latency = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "samples": n_lat}
+    copy_gbps = measured_copy_gbps(torch)
+    log(f"per-block latency p10/p50/p90 {latency['p10']}/{latency['p50']}/{latency['p90']} us; "
+        f"device copy {copy_gbps:.0f} GB/s")
 
     # ----------------------------------------- per-stage device time (live) --
     stage_names = {M.STAGE_SELECT: "select_permute", M.STAGE_GATEUP: "gateup_swiglu",
@@ -297,7 +344,10 @@ def main():
         "throughput": {"blocks_per_s": round(1e6 / us_block, 1),
                        "verify_nodes_per_s": round(cfg.N * 1e6 / us_block, 1),
                        "unique_expert_GBps": round(uniq_gbps, 1),
-                       "unique_expert_frac_of_peak": round(uniq_gbps / HBM_PEAK_GBPS, 4)},
+                       "unique_expert_frac_of_peak": round(uniq_gbps / HBM_PEAK_GBPS, 4),
+                       "copy_GBps": round(copy_gbps, 1),
+                       "unique_expert_frac_of_copy": round(uniq_gbps / copy_gbps, 4)},
+        "latency_us": latency,
         "selection": {"U_mean": statistics.mean(U), "U_by_block": U,
                       "eligible_mean": statistics.mean(st["n_eligible"] for st in stats),
                       "natural_union_mean": statistics.mean(st["n_natural_union"] for st in stats),
@@ -527,22 +577,10 @@ def offload_sweep(args):
                       "expert_bytes": per_expert, "modes": results}), flush=True)
 
 
-def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):
-    """Microseconds per block and active experts of selector variants on the
-    same kernels, weights and blocks: natural routing (every expert
-    eligible), AcceptMoE (self-sized), AcceptMoE-B and MoE-Spec at the same
-    fixed budgets (B = AcceptMoE's mean U, and 16), and the full-softmax
-    reading of the demand.  Each is graph-replayed like the headline run."""
-    B = max(1, int(round(u_mean)))
-    base = layers[0].shape
-    spec = M.F_UNIT_COMMIT | M.F_NO_ANCHOR
-    plan = [("natural", dict(flags=base.flags | M.F_NATURAL)),
-            ("acceptmoe", dict()),
-            (f"acceptmoe_b{B}", dict(fixed_budget=B)),
-            (f"moe_spec_b{B}", dict(flags=base.flags | spec, fixed_budget=B)),
-            ("acceptmoe_b16", dict(fixed_budget=16)),
-            ("moe_spec_b16", dict(flags=base.flags | spec, fixed_budget=16)),
-            ("full_softmax_demand", dict(flags=base.flags | M.F_DEMAND_FULL))]
+def time_variants(M, torch, layers, dblocks, slots, S, steps, plan):
+    """For each (name, shape fields) of `plan`: the layers' variants over the
+    rotation slots, graph-replayed `steps` times; us per block and the mean
+    selection statistics."""
     res = {}
     for name, fields in plan:
         vl = [layer.variant(**fields) for layer in layers]
@@ -586,6 +624,55 @@ def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):
                      "eligible_mean": statistics.mean(x["n_eligible"] for x in st),
                      "budget": fields.get("fixed_budget", 0)}
         del graphs
+    return res
+
+
+def budget_sweep(M, torch, cfg, layers, dblocks, slots, S, steps):
+    """[EcoSpec, Fig. 1]: verification time grows linearly with the number of
+    active experts.  AcceptMoE-B with B = 8, 16, .., 128 on the same blocks and
+    weights; prints us per block against U and the least-squares line
+    us = a + b * U (b: us per active expert, next to the time to stream one
+    expert's weights at 8 TB/s)."""
+    plan = [(f"b{B}", dict(fixed_budget=B)) for B in range(8, cfg.E + 1, 8)]
+    res = time_variants(M, torch, layers, dblocks, slots, S, steps, plan)
+    xs = [r["U_mean"] for r in res.values()]
+    ys = [r["us_per_block"] for r in res.values()]
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    a = my - b * mx
+    ss_res = sum((y - (a + b * x)) ** 2 for x, y in zip(xs, ys))
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    for name, r in res.items():
+        log(f"{name}: U {r['U_mean']:.2f} -> {r['us_per_block']:.2f} us")
+    expert_us = cfg.expert_bytes() / (HBM_PEAK_GBPS * 1e9) * 1e6
+    print(json.dumps({"sweep": "fixed_budget_linearity", "workload": f"{cfg.name}: E={cfg.E} "
+                      f"k={cfg.k} H={cfg.H} I={cfg.I} N={cfg.N}, {cfg.w} experts, AcceptMoE-B",
+                      "points": [{"B": r["budget"], "U": r["U_mean"], "us": r["us_per_block"]}
+                                 for r in res.values()],
+                      "fit": {"us_at_U0": round(a, 2), "us_per_expert": round(b, 3),
+                              "r2": round(1 - ss_res / ss_tot, 5),
+                              "expert_stream_us_at_8TBps": round(expert_us, 3)}}), flush=True)
+
+
+def selector_variants(M, torch, layers, dblocks, slots, S, u_mean, steps):
+    """Microseconds per block and active experts of selector variants on the
+    same kernels, weights and blocks: natural routing (every expert
+    eligible), AcceptMoE (self-sized), AcceptMoE-B and MoE-Spec at the same
+    fixed budgets (B = AcceptMoE's mean U, and 16), and the full-softmax
+    reading of the demand.  Each is graph-replayed like the headline run."""
+    B = max(1, int(round(u_mean)))
+    base = layers[0].shape
+    spec = M.F_UNIT_COMMIT | M.F_NO_ANCHOR
+    plan = [("natural", dict(flags=base.flags | M.F_NATURAL)),
+            ("acceptmoe", dict()),
+            (f"acceptmoe_b{B}", dict(fixed_budget=B)),
+            (f"moe_spec_b{B}", dict(flags=base.flags | spec, fixed_budget=B)),
+            ("acceptmoe_b16", dict(fixed_budget=16)),
+            ("moe_spec_b16", dict(flags=base.flags | spec, fixed_budget=16)),
+            ("full_softmax_demand", dict(flags=base.flags | M.F_DEMAND_FULL))]
+    res = time_variants(M, torch, layers, dblocks, slots, S, steps, plan)
     nat = res["natural"]["us_per_block"]
     for v in res.values():
         v["speedup_vs_natural"] = round(nat / v["us_per_block"], 4)
