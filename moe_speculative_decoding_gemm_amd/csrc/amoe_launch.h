@@ -50,6 +50,7 @@ struct SelectArgs {
   int32_t* n_active;
   int32_t* max_rows;  // or null: the most rows routed to one expert
   int32_t* groups;    // or null: the active experts' 64-row groups (see permute_block)
+  int32_t* active_w;  // or null: the active experts in work order (see permute_block)
 };
 
 // router product, per-node softmax / natural top-k / demand terms, set
@@ -106,6 +107,10 @@ struct GroupedArgs {
   // read the item's weights at about the same time
   const int32_t* max_rows;
   const int32_t* groups;
+  // bf16 / fp8: the active list is in work order (heaviest cost class first,
+  // see permute_block): a grid of whole rounds of one work-group per CU
+  // deals the items in a snake over the rounds
+  int snake;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);

@@ -59,6 +59,10 @@ struct PermuteSmem {
   int apos[kMaxE];
   int run[kMaxE];
   int w[NTHR / kWave][kMaxE];
+  int wpos[kMaxE];  // position in the work order (active_w)
+  int cls[kMaxE];   // cost class flags, packed (see the work order)
+  int cpos[kMaxE];  // their exclusive scan
+  int ctot;
   int ng[kMaxE];  // 64-row groups of each expert
   int gs[kMaxE];  // their exclusive scan
   int nact, ngrp;
@@ -74,7 +78,8 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
                                               int32_t* active, int32_t* n_active,
                                               const uint8_t* resident, StatsDev* stats,
                                               PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
-                                              int32_t* groups = nullptr) {
+                                              int32_t* groups = nullptr,
+                                              int32_t* active_w = nullptr) {
   constexpr int NW = NTHR / kWave;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
@@ -87,8 +92,12 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
   __syncthreads();
   if (t < E) {
-    sm.flag[t] = sm.cnt[t] > 0 ? 1 : 0;
-    sm.ng[t] = (sm.cnt[t] + 63) >> 6;
+    const int c = sm.cnt[t];
+    sm.flag[t] = c > 0 ? 1 : 0;
+    sm.ng[t] = (c + 63) >> 6;
+    // cost class of the expert's work items (activation rows staged per
+    // chunk: 64 / 32 / 16), one 10-bit count field each
+    sm.cls[t] = c > 32 ? 1 : (c > 16 ? (1 << 10) : (c > 0 ? (1 << 20) : 0));
   }
   __syncthreads();
   if (wave == 0) {
@@ -98,13 +107,30 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   } else if (wave == 1 && groups) {
     const int ng = wave_exclusive_scan_256(sm.ng, sm.gs, E);
     if (lane == 0) sm.ngrp = ng;
+  } else if (wave == 2 && active_w) {
+    const int ct = wave_exclusive_scan_256(sm.cls, sm.cpos, E);
+    if (lane == 0) sm.ctot = ct;
   }
   __syncthreads();
-  // the 64-row groups of the active experts in active order, as
-  // (active index << 16 | group): groups[0] = count, groups[1 + g] = entry g
+  // work order: the active experts by cost class, the class that stages 64
+  // rows first, then 32, then 16, each class in index order; without
+  // active_w it is the active order
+  if (t < E) {
+    int wp = sm.apos[t];
+    if (active_w && sm.flag[t]) {
+      const int c = sm.cnt[t], cp = sm.cpos[t], ct = sm.ctot;
+      const int n64 = ct & 1023, n32 = (ct >> 10) & 1023;
+      wp = c > 32 ? (cp & 1023) : (c > 16 ? n64 + ((cp >> 10) & 1023) : n64 + n32 + (cp >> 20));
+      active_w[wp] = t;
+    }
+    sm.wpos[t] = wp;
+  }
+  // the 64-row groups of the active experts in work order, as
+  // (work index << 16 | group): groups[0] = count, groups[1 + g] = entry g
   if (groups) {
+    __syncthreads();
     if (t < E) {
-      const int n = sm.ng[t], base = sm.gs[t], u = sm.apos[t];
+      const int n = sm.ng[t], base = sm.gs[t], u = sm.wpos[t];
       for (int j = 0; j < n; ++j) groups[1 + base + j] = (u << 16) | j;
     }
     if (t == 0) groups[0] = sm.ngrp;

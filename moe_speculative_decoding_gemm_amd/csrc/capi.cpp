@@ -155,6 +155,7 @@ struct VerifyWs {
   int32_t* active;
   int32_t* n_active;
   int32_t* groups;
+  int32_t* active_w;
   acceptmoe_stats* stats;
   void* h_perm;
   float* y_perm;
@@ -181,6 +182,8 @@ VerifyWs carve_verify(Carver& c, const acceptmoe_shape* s, bool shared) {
   w.n_active = c.take<int32_t>(2);  // [1]: the most rows routed to one expert
   // 64-row groups of the active experts: at most N*k/64 + E, plus the count
   w.groups = c.take<int32_t>(2 + NK / 64 + s->E);
+  // the active experts in the order the expert kernels take them
+  w.active_w = c.take<int32_t>(s->E);
   w.stats = c.take<acceptmoe_stats>(1);
   w.h_perm = c.take<char>(NK * s->I * hidden_elem_bytes(s->w_dtype));
   w.y_perm = c.take<float>(NK * s->H);
@@ -568,6 +571,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   a.n_wslots = 0;
   a.max_rows = nullptr;
   a.groups = nullptr;
+  a.snake = 0;
   return hip_status(amoe::launch_grouped(a, stream), "moe_grouped_swiglu");
 }
 
@@ -685,6 +689,7 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.n_active = w.n_active;
   a.max_rows = w.n_active + 1;
   a.groups = w.groups;
+  a.active_w = w.active_w;
   timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
   rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
   if (rc) return rc;
@@ -709,7 +714,11 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.s2 = in->s2;
   g.offsets = w.offsets;
   g.sorted_assign = w.sorted_assign;
-  g.active = active;
+  // the expert kernels take the active experts most-routed first: the work
+  // items of the few experts with many rows (the longest ones) then start on
+  // separate CUs, and the lightest items are the ones that share a CU last
+  g.active = w.active_w;
+  g.snake = 1;
   g.n_active = w.n_active;
   g.y_perm = w.y_perm;
   g.h_perm = w.h_perm;
@@ -729,6 +738,7 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     // row-group table indexes the full active list: not used for the two lists)
     const int32_t* lists = cache->dev_lists;
     g.groups = nullptr;
+    g.snake = 0;
     g.active = lists;
     g.n_active = lists + s->E;
     rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");
@@ -773,6 +783,7 @@ static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     gs.w_slot = nullptr;
     gs.max_rows = nullptr;
     gs.groups = nullptr;
+    gs.snake = 0;
     gs.n_wslots = 0;
     gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
     rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");

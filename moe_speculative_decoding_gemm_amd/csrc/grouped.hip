@@ -451,7 +451,20 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
   // its weights at about the same time).
   const bool by_group = a.groups != nullptr && a.max_rows != nullptr && *a.max_rows > ROWS;
   const int n_units = by_group ? a.groups[0] * tiles : n_items * R;
-  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  // snake: the active list comes heaviest first and the grid is whole rounds
+  // of one work-group per CU (work-group b, b + C, b + 2C, .. share CU b % C
+  // under the in-order dispatch), so the first round takes ranks 0..C-1 in
+  // order and every later round runs backwards: the CU with the heaviest
+  // first item gets the lightest items of the later rounds
+  const int C = a.num_cu;
+  const bool snake = a.snake && !by_group && C > 0 && gridDim.x % C == 0;
+  for (int base = 0; base < n_units; base += gridDim.x) {
+    int unit = base + static_cast<int>(blockIdx.x);
+    if (snake && base == 0) {
+      const int q = unit / C, p = unit - q * C;
+      unit = q == 0 ? p : q * C + (C - 1 - p);
+    }
+    if (unit >= n_units) continue;
     int u, tile, g0, rstep;
     if (by_group) {
       const int gi = unit / tiles;

@@ -606,7 +606,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   if (a.counts)
     permute_block<kTail>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
                        a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
-                       sm.u.perm, a.max_rows, a.groups);
+                       sm.u.perm, a.max_rows, a.groups, a.active_w);
 }
 
 // commit[depth] and the parent's depth of node `node` (of any wave: clamped
@@ -857,7 +857,7 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
     if (last_block_done(&a.counters[1], gridDim.x))
       permute_block<256>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
                          a.inv_pos, a.active, a.n_active, a.resident,
-                         static_cast<StatsDev*>(a.stats), perm, a.max_rows, a.groups);
+                         static_cast<StatsDev*>(a.stats), perm, a.max_rows, a.groups, a.active_w);
   }
 }
 
