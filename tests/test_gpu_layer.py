@@ -261,3 +261,45 @@ def test_selector_variant_layer(lib, vname, flags, budget):
         ref = oracle_layer(cfg, b, w, out["logits_out"].cpu().numpy())
         assert check_selection(out, ref, st, cfg, f"{vname} seed {seed}")
         assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("budget", [6, 10, 20], ids=["b6", "b10", "b20"])
+def test_work_order_rounds_match_separate_path(lib, budget):
+    """verify_block hands the expert kernels the active experts heaviest
+    cost class first and deals the work items over the per-CU rounds in a
+    snake (on 256 CUs: one round and part of a second, two and part of a
+    third, more items than one pass: U = 6, 10, 14 active experts of 64
+    gate/up items each);
+    the standalone grouped call takes the ascending active list with the
+    plain order.  Both must give the same bits, and y must be within the bf16
+    tolerance of the oracle."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=32, k=2, H=256, I=2048, N=64, fixed_budget=budget)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 3)
+    say(f"work order B={budget}")
+    out, st = run_layer(lib, cfg, b, w, pack=True)
+    ref = oracle_layer(cfg, b, w, out["logits_out"].cpu().numpy())
+    assert check_selection(out, ref, st, cfg, f"work order B={budget}")
+    assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+    # the same selection through the separate entry points
+    N, H, I, E, k = cfg.N, cfg.H, cfg.I, cfg.E, cfg.k
+    dev = "cuda"
+    e_ = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
+    ti, tg = out["topk_idx"], out["topk_gate"]
+    counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)
+    lib.moe_route_permute(N, k, E, ti, counts, offsets, sa, ip, act, na)
+    w13, w2 = lib.pack_experts(shape_of(lib, cfg, w_layout=lib.LAYOUT_PACKED), w["w13"], w["w2"], E)
+    y_perm = e_(N * k, H, dt=torch.float32)
+    gws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, k, I, 1), dtype=torch.uint8,
+                      device=dev)
+    d = upload_block(b)
+    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 1, d["x"], w13, w2, None, None, offsets, sa, act,
+                           na, y_perm, gws, w_layout=lib.LAYOUT_PACKED)
+    y = e_(N, H, dt=torch.bfloat16)
+    lib.moe_combine(N, k, H, 1, y_perm, ip, tg, None, y)
+    torch.cuda.synchronize()
+    u = int(na.item())
+    rows = counts.cpu().numpy()[act.cpu().numpy()[:u]]
+    say(f"  U={u} rows per active expert {sorted(rows.tolist(), reverse=True)}")
+    assert u == st["n_active"] and rows.max() <= 64
+    assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
