@@ -7,8 +7,12 @@ A step is one whole verify block (router -> selection -> permute -> grouped
 SwiGLU over the unique active experts -> combine) on one seeded synthetic
 64-node draft tree, with every input already resident in HBM.  Steps rotate
 over 8 seeded blocks and 4 independently drawn layer weight sets so that no
-expert weights can be served from the 256 MB Infinity Cache; each rotation
-slot is captured once in a HIP graph and replayed.
+expert weights can be served from the 256 MB Infinity Cache.  The 8 rotation
+slots are captured in sequence in one HIP graph (one pass over a stack of
+MoE layers, as a model forward captured whole runs them); the timed K steps
+are whole replays of it plus single-slot graph replays for the remainder.
+The same K steps as one graph per block (a graph launch in front of every
+block) are reported beside the value.
 
 Prints one JSON line: microseconds per verify block (lower is better), the
 achieved HBM bandwidth on unique-expert weight bytes, the roofline of the
@@ -228,6 +232,21 @@ def main():
             bi, li = slots[s]
             if not torch.equal(layers[li].out["y"].view(torch.uint8), y_eager[s].view(torch.uint8)):
                 raise RuntimeError(f"graph replay of slot {s} differs from eager")
+        # all S slots in sequence in one graph: one pass over a stack of MoE
+        # layers, as a model forward captured whole runs them (no graph
+        # launch between layers)
+        stack = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(stack):
+            for s in range(S):
+                run_slot(s)
+        torch.cuda.synchronize()
+        stack.replay()
+        torch.cuda.synchronize()
+        for s in range(S):  # the last slot that writes each layer's outputs
+            bi, li = slots[s]
+            if s + len(layers) >= S and not torch.equal(layers[li].out["y"].view(torch.uint8),
+                                                        y_eager[s].view(torch.uint8)):
+                raise RuntimeError(f"stacked graph replay of slot {s} differs from eager")
 
     def step(i):
         s = i % S
@@ -236,21 +255,37 @@ def main():
         else:
             run_slot(s)
 
+    def timed(n, stacked):
+        """n steps (blocks) between two events: whole stack replays, then
+        single-block replays for the rest (or single blocks only)"""
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record()
+        done = 0
+        if stacked:
+            while done + S <= n:
+                stack.replay()
+                done += S
+        while done < n:
+            step(done)
+            done += 1
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b), time.perf_counter() - t0
+
     # -------------------------------------------------------- timed region --
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = e0.elapsed_time(e1)
+    # single-block graphs first (reported beside the value), then the timed
+    # steps proper: stacked graphs when captured
+    us_single = None
+    if graphs:
+        ms_single, _ = timed(args.steps, False)
+        us_single = ms_single / args.steps * 1e3
+    ms_total, wall = timed(args.steps, bool(graphs))
     ms_per_step = ms_total / args.steps
     us_block = ms_per_step * 1e3
     bytes_per_step = statistics.mean(uniq_bytes[i % S] for i in range(args.steps))
@@ -339,7 +374,8 @@ def main():
         "config": {"workload": f"{cfg.name}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} "
                                f"N={cfg.N}-node tree, {cfg.act} act / {cfg.w} experts",
                    "layers_rotated": args.layers, "blocks_rotated": args.blocks,
-                   "launch": "eager" if args.eager else "hip-graph replay",
+                   "launch": "eager" if args.eager else
+                   f"hip-graph replay, {S} blocks per graph (a stack of MoE layers)",
                    "flags": cfg.flags, "fixed_budget": cfg.fixed_budget},
         "throughput": {"blocks_per_s": round(1e6 / us_block, 1),
                        "verify_nodes_per_s": round(cfg.N * 1e6 / us_block, 1),
@@ -348,6 +384,7 @@ def main():
                        "copy_GBps": round(copy_gbps, 1),
                        "unique_expert_frac_of_copy": round(uniq_gbps / copy_gbps, 4)},
         "latency_us": latency,
+        "us_per_block_one_graph_per_block": None if us_single is None else round(us_single, 3),
         "selection": {"U_mean": statistics.mean(U), "U_by_block": U,
                       "eligible_mean": statistics.mean(st["n_eligible"] for st in stats),
                       "natural_union_mean": statistics.mean(st["n_natural_union"] for st in stats),
@@ -579,7 +616,8 @@ def offload_sweep(args):
 
 def time_variants(M, torch, layers, dblocks, slots, S, steps, plan):
     """For each (name, shape fields) of `plan`: the layers' variants over the
-    rotation slots, graph-replayed `steps` times; us per block and the mean
+    rotation slots, captured in sequence in one graph (as the headline
+    value) and replayed for about `steps` blocks; us per block and the mean
     selection statistics."""
     res = {}
     for name, fields in plan:
@@ -602,28 +640,26 @@ def time_variants(M, torch, layers, dblocks, slots, S, steps, plan):
                 run_v(s)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        graphs = []
-        for s in range(S):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        stack = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(stack):
+            for s in range(S):
                 run_v(s)
-            graphs.append(g)
-        for i in range(S):
-            graphs[i].replay()
+        stack.replay()
         torch.cuda.synchronize()
+        reps = max(1, steps // S)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(steps):
-            graphs[i % S].replay()
+        for _ in range(reps):
+            stack.replay()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = e0.elapsed_time(e1) * 1e3 / (reps * S)
         res[name] = {"us_per_block": round(us, 3),
                      "U_mean": statistics.mean(x["n_active"] for x in st),
                      "eligible_mean": statistics.mean(x["n_eligible"] for x in st),
                      "budget": fields.get("fixed_budget", 0)}
-        del graphs
+        del stack
     return res
 
 
