@@ -2,8 +2,9 @@
 // device function run by one work-group of 256 or 1024 threads.
 //
 // Pass 1 is an LDS histogram (integer atomics: the counts do not depend on
-// their order).  One wave scans the counts into offsets and compacts the
-// active experts.  Pass 2 scatters in rounds of 1024 assignments: inside a
+// their order).  One wave scans the counts into offsets while another
+// compacts the active experts (and two more, when asked, scan the 64-row
+// groups and the cost classes of the work order).  Pass 2 scatters in rounds of 1024 assignments: inside a
 // wave, lanes with the same expert find each other with eight ballots over
 // the expert-id bits and take their rank from a popcount of the lower peers;
 // per-wave totals are scanned across the waves in wave order.  Ranks
@@ -102,6 +103,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   __syncthreads();
   if (wave == 0) {
     wave_exclusive_scan_256(sm.cnt, sm.off, E);
+  } else if (wave == 3) {
     const int na = wave_exclusive_scan_256(sm.flag, sm.apos, E);
     if (lane == 0) sm.nact = na;
   } else if (wave == 1 && groups) {
@@ -127,8 +129,8 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   }
   // the 64-row groups of the active experts in work order, as
   // (work index << 16 | group): groups[0] = count, groups[1 + g] = entry g
+  // (thread t reads only the work position it wrote)
   if (groups) {
-    __syncthreads();
     if (t < E) {
       const int n = sm.ng[t], base = sm.gs[t], u = sm.wpos[t];
       for (int j = 0; j < n; ++j) groups[1 + base + j] = (u << 16) | j;

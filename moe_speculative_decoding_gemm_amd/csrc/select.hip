@@ -108,11 +108,12 @@ struct NodeSmem {
 };
 struct SetSmem {
   double d[kMaxE];
+  double dl[kMaxE];  // d ln d (0 for d = 0)
   double key[kMaxE];
   int anchor[kMaxE], rank[kMaxE], elig[kMaxE];
   int part[kTail];  // split_rank partial counts
-  int err, na, nnat, nsel, ncand;
-  double tot, h;
+  int err, na, nnat, nsel, ncand, take;
+  double tot, r_eff;
 };
 struct TailSmem {
   SetSmem set;
@@ -350,8 +351,8 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     sm.nsel = 0;
     sm.ncand = 0;
   }
-  __syncthreads();
-  // error words and the commit table, loaded together with the demand rows
+  // error words and the commit table, loaded together with the demand rows;
+  // the loads go out before the barrier that publishes the counters above
   const int err0 = t < nwg ? a.e_part[t] : 0;
   const float com0 = t < a.n_depth ? a.commit[t] : 0.f;
   // demand per expert: its row of group partials summed in group order
@@ -378,12 +379,21 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
       for (int u = 0; u < 16; ++u)
         if (w0 + u < nwg) f |= static_cast<int>((fv[u >> 2] >> (8 * (u & 3))) & 0xffu);
     }
+  }
+  __syncthreads();
+  if (t < E) {
     if (f & 1) atomicAdd(&sm.na, 1);
     if (f & 2) atomicAdd(&sm.nnat, 1);
   }
   if (t < kMaxE) {
+    const bool in_fill = t < E && !(f & 1);  // experts that take part in the fill
     sm.d[t] = dsum;
+    sm.dl[t] = dsum > 0.0 ? dsum * log(dsum) : 0.0;
     sm.anchor[t] = f & 1;
+    // fill order: (demand desc, index asc) over the non-anchor experts;
+    // anchors and padding carry demand -1, below every real demand
+    sm.key[t] = in_fill ? dsum : -1.0;
+    sm.elig[t] = in_fill;
   }
   if (err0) atomicOr(&sm.err, err0);
   for (int w = t + kTail; w < nwg; w += kTail) {
@@ -396,41 +406,35 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     if (!(c >= 0.f) || isinf(c)) atomicOr(&sm.err, kErrCommit);
   }
   __syncthreads();
-  if (t < kWave) {  // wave 0: total demand and entropy, fixed order
-    double sd = 0.0;
-    for (int e = t; e < E; e += kWave) sd += sm.d[e];
+  if (t < kWave) {  // wave 0: total demand, entropy and the set size
+    // H = -sum q ln q with q = d / tot equals ln tot - (sum d ln d) / tot;
+    // each expert's d ln d was taken with its demand sum
+    double sd = 0.0, sl = 0.0;
+    for (int e = t; e < E; e += kWave) {
+      sd += sm.d[e];
+      sl += sm.dl[e];
+    }
     const double tot = wave_sum_f64(sd);
-    double h = 0.0;
-    if (tot > 0.0) {
-      for (int e = t; e < E; e += kWave) {
-        const double dv = sm.d[e];
-        if (dv > 0.0) {
-          const double q = dv / tot;
-          h -= q * log(q);
-        }
-      }
-    }
-    h = wave_sum_f64(h);
+    const double sdl = wave_sum_f64(sl);
     if (t == 0) {
+      const double h = tot > 0.0 ? log(tot) - sdl / tot : 0.0;
+      const double r_eff = tot > 0.0 ? exp(h) : 0.0;
+      const int n_min = max(k, a.min_set);
+      const int n_raw = a.fixed_budget > 0 ? a.fixed_budget : static_cast<int>(floor(r_eff + 0.5));
+      const int n = min(E, max(max(n_raw, sm.na), n_min));
       sm.tot = tot;
-      sm.h = h;
+      sm.r_eff = r_eff;
+      sm.take = n - sm.na;
     }
   }
-  // fill order: (demand desc, index asc) over the non-anchor experts; anchors
-  // and padding carry demand -1, below every real demand
-  if (t < kMaxE) {
-    sm.key[t] = (t < E && !sm.anchor[t]) ? sm.d[t] : -1.0;
-    sm.elig[t] = t < E && !sm.anchor[t];  // experts that take part in the fill
-  }
-  __syncthreads();
+  // the fill ranks do not depend on the set size: counted while wave 0 sizes
+  // the set (split_rank's barrier publishes both)
+  const int fill_rank = split_rank(sm.key, sm.part, E, true, sm.elig);
   const double tot = sm.tot;
-  const double r_eff = tot > 0.0 ? exp(sm.h) : 0.0;
+  const double r_eff = sm.r_eff;
   const int n_anchor = sm.na;
   const int n_min = max(k, a.min_set);
-  const int n_raw = a.fixed_budget > 0 ? a.fixed_budget : static_cast<int>(floor(r_eff + 0.5));
-  const int n = min(E, max(max(n_raw, n_anchor), n_min));
-  const int take = n - n_anchor;
-  const int fill_rank = split_rank(sm.key, sm.part, E, true, sm.elig);
+  const int take = sm.take;
   int el = 0;
   if (t < E) {
     el = natural ? 1 : (sm.anchor[t] || fill_rank < take) ? 1 : 0;
