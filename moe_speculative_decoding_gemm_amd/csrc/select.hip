@@ -51,6 +51,7 @@ constexpr int kFusedMaxN = 256;  // largest N whose restricted top-k runs in the
 constexpr int kKeyCap = 4096;    // (node, member) keys per rank-counting pass
 constexpr int kLgCap = 8192;     // logits the tail holds in LDS (N * E up to this)
 constexpr int kTail = 1024;      // threads of the tail kernel (one work-group)
+constexpr int kRankCountMax = 64;  // largest (padded) set whose restricted top-k counts ranks
 
 // demand / flag partial rows are stored expert-major, one row of group
 // partials per expert, padded so that a row starts 16-byte aligned
@@ -505,15 +506,29 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   const int nm = sm.nmem, nneedy = sm.nneedy;
   // Small sets: rank counting over (needy node, member) keys, rows padded to
   // a multiple of 4 with key 0 (below every key), as many nodes per pass as
-  // fit.  Large sets (more than 64 members; the counting costs members^2 per
-  // node): one wave per needy node takes k rounds of a wave max over the
-  // keys of the eligible experts.  Both give each node's top-k keys in key
-  // order (value, then lower index).
+  // fit.  Large sets (more than kRankCountMax members; the counting costs
+  // members^2 per node): one wave per needy node keeps the node's natural
+  // top-k members of the set and takes the remaining places by rounds of a
+  // wave max over the set's other experts.  Both give each node's top-k keys
+  // in key order (value, then lower index).
   const int nmp = (nm + 3) & ~3;
-  if (nmp > 64) {
+  if (nmp > kRankCountMax) {
     constexpr int NWV = kTail / kWave;
     for (int c = wave; c < nneedy; c += NWV) {
       const int i = sm.needy[c];
+      // The node's natural top-k members of the set hold the set's largest
+      // keys (the natural top-k are the largest of all experts), so they keep
+      // their places, in order; only the k - kept places after them take
+      // rounds of a wave max, over the set's other experts.
+      int my_e = 0;
+      float my_l = 0.f;
+      if (lane < k) {
+        my_e = sm.top_e[i * k + lane];
+        my_l = sm.top_l[i * k + lane];
+      }
+      const bool keep = lane < k && sm.set.elig[my_e] != 0;
+      const uint64_t km = __ballot(keep);
+      const int kept = __popcll(km);
       uint64_t key[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -522,7 +537,20 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
         const float v = lg_lds ? sm.lg[i * E + ec] : a.logits[static_cast<size_t>(i) * E + ec];
         key[q] = (e < E && sm.set.elig[ec]) ? topk_key(v, ec) : 0ull;
       }
-      for (int j = 0; j < k; ++j) {
+      for (int j = 0; j < k; ++j) {  // natural top-k experts are not candidates
+        const int ej = __builtin_amdgcn_readlane(my_e, j);
+        if ((ej & (kWave - 1)) == lane) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == (ej >> 6)) key[q] = 0ull;
+        }
+      }
+      if (keep) {
+        const int pos = __popcll(km & ((1ull << lane) - 1ull));
+        sm.top_e[i * k + pos] = my_e;
+        sm.top_l[i * k + pos] = my_l;
+      }
+      for (int j = kept; j < k; ++j) {
         uint64_t b = key[0];
 #pragma unroll
         for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
@@ -543,7 +571,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   }
   const int per = max(1, kKeyCap / max(nmp, 4));
   const float inv = 1.0f / static_cast<float>(max(nmp, 1));
-  for (int c0 = 0; nmp <= 64 && c0 < nneedy; c0 += per) {
+  for (int c0 = 0; nmp <= kRankCountMax && c0 < nneedy; c0 += per) {
     const int cn = min(per, nneedy - c0);
     const int total = cn * nmp;
     for (int x = t; x < total; x += kTail) {
