@@ -852,14 +852,37 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
   if (i < a.N) {
     const int E = a.E, k = a.k;
     const float* row = a.logits + static_cast<size_t>(i) * E;
+    // the node's natural top-k members of the set keep their places, in
+    // order (they hold the set's largest keys); the remaining places take
+    // rounds of a wave max over the set's other experts
+    int nat_e = 0;
+    if (lane < k) nat_e = clamp_expert(a.nat_idx[static_cast<size_t>(i) * k + lane], E);
+    const bool keep = lane < k && a.eligible[nat_e] != 0;
+    const uint64_t km = __ballot(keep);
+    const int kept = __popcll(km);
+    int my_sel = 0;
+    for (int j = 0, pos = 0; j < k; ++j) {  // slot pos < kept: the pos-th kept natural expert
+      if ((km >> j) & 1ull) {
+        const int ej = __builtin_amdgcn_readlane(nat_e, j);
+        if (lane == pos) my_sel = ej;
+        ++pos;
+      }
+    }
     uint64_t key[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + kWave * q;
       key[q] = (e < E && a.eligible[e]) ? topk_key(row[e], e) : 0ull;
     }
-    int my_sel = 0;
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < k; ++j) {  // natural top-k experts are not candidates
+      const int ej = __builtin_amdgcn_readlane(nat_e, j);
+      if ((ej & (kWave - 1)) == lane) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q == (ej >> 6)) key[q] = 0ull;
+      }
+    }
+    for (int j = kept; j < k; ++j) {
       uint64_t b = key[0];
 #pragma unroll
       for (int q = 1; q < 4; ++q) b = key[q] > b ? key[q] : b;
