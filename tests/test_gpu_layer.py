@@ -67,6 +67,10 @@ SMALL = [
     # separate units next to each other
     ("qwen3_30b", dict(E=12, k=4, H=256, I=320, N=300)),
     ("dsv31", dict(E=10, k=3, H=256, I=256, N=200, n_chains=25, chain_len=8)),
+    # the largest sizes: 4096 nodes (thousands of rows per expert, dozens of
+    # 64-row groups each), and 256 experts with top-16
+    ("qwen3_30b", dict(E=16, k=8, H=128, I=128, N=4096)),
+    ("qwen3_30b", dict(E=256, k=16, H=128, I=128, N=64)),
 ]
 
 
