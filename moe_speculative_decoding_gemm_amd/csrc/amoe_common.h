@@ -89,6 +89,25 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
 }
 
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele steps inside each
+// 16-lane row with DPP row shifts (lanes shifted in from outside the row
+// read 0), then the totals of the rows below added from three readlanes.
+// Integer adds: exact, so the order does not matter.
+template <int SHR>
+__device__ __forceinline__ uint32_t row_shr_zero(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x110 + SHR, 0xf, 0xf, true));
+}
+__device__ __forceinline__ uint32_t wave_inclusive_sum_u32(uint32_t v) {
+  v += row_shr_zero<1>(v);
+  v += row_shr_zero<2>(v);
+  v += row_shr_zero<4>(v);
+  v += row_shr_zero<8>(v);
+  const uint32_t r0 = readlane_u32(v, 15), r1 = readlane_u32(v, 31), r2 = readlane_u32(v, 47);
+  const int row = (static_cast<int>(threadIdx.x) & (kWave - 1)) >> 4;
+  return v + (row == 0 ? 0u : (row == 1 ? r0 : (row == 2 ? r0 + r1 : r0 + r1 + r2)));
+}
+
 template <int CTRL>
 __device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
   const uint32_t oh = dpp_mov<CTRL>(hi), ol = dpp_mov<CTRL>(lo);

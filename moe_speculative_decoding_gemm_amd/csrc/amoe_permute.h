@@ -36,19 +36,14 @@ __device__ __forceinline__ int wave_exclusive_scan_256(const int* v, int* out, i
     loc[q] = s;
     s += idx < n ? v[idx] : 0;
   }
-  int inc = s;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(inc, d, kWave);
-    if (lane >= d) inc += o;
-  }
+  const int inc = static_cast<int>(wave_inclusive_sum_u32(static_cast<uint32_t>(s)));
   const int base = inc - s;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = lane * 4 + q;
     if (idx < n) out[idx] = base + loc[q];
   }
-  return __shfl(inc, kWave - 1, kWave);
+  return static_cast<int>(readlane_u32(static_cast<uint32_t>(inc), kWave - 1));
 }
 
 // LDS of permute_block for NTHR threads
@@ -156,8 +151,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     int nr = 0;
     if (resident)
       for (int e = t; e < E; e += kWave) nr += (sm.flag[e] && !resident[e]) ? 1 : 0;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) nr += __shfl_xor(nr, m, kWave);
+    nr = static_cast<int>(readlane_u32(wave_inclusive_sum_u32(static_cast<uint32_t>(nr)), kWave - 1));
     if (t == 0) {
       stats->n_active = sm.nact;
       stats->n_active_nonresident = nr;
