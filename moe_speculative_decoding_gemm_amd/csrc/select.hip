@@ -514,8 +514,24 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   const int nmp = (nm + 3) & ~3;
   if (nmp > kRankCountMax) {
     constexpr int NWV = kTail / kWave;
+    // a node's logits (from memory when they do not fit in LDS) are loaded
+    // one node ahead, so their latency hides behind the previous node's rounds
+    float lv[4];
+    auto load_logits = [&](int c, float (&v)[4]) {
+      const int i = sm.needy[c < nneedy ? c : 0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ec = min(lane + kWave * q, E - 1);
+        v[q] = lg_lds ? sm.lg[i * E + ec] : a.logits[static_cast<size_t>(i) * E + ec];
+      }
+    };
+    if (wave < nneedy) load_logits(wave, lv);
     for (int c = wave; c < nneedy; c += NWV) {
       const int i = sm.needy[c];
+      float cur[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = lv[q];
+      if (c + NWV < nneedy) load_logits(c + NWV, lv);
       // The node's natural top-k members of the set hold the set's largest
       // keys (the natural top-k are the largest of all experts), so they keep
       // their places, in order; only the k - kept places after them take
@@ -534,8 +550,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
       for (int q = 0; q < 4; ++q) {
         const int e = lane + kWave * q;
         const int ec = e < E ? e : E - 1;
-        const float v = lg_lds ? sm.lg[i * E + ec] : a.logits[static_cast<size_t>(i) * E + ec];
-        key[q] = (e < E && sm.set.elig[ec]) ? topk_key(v, ec) : 0ull;
+        key[q] = (e < E && sm.set.elig[ec]) ? topk_key(cur[q], ec) : 0ull;
       }
       for (int j = 0; j < k; ++j) {  // natural top-k experts are not candidates
         const int ej = __builtin_amdgcn_readlane(my_e, j);
