@@ -82,7 +82,11 @@ enum {
   ACCEPTMOE_ERR_BAD_TREE = 1u << 0,  /* parent not an earlier node, or depth != parent's + 1 */
   ACCEPTMOE_ERR_DEPTH = 1u << 1,     /* depth outside [0, n_depth)                          */
   ACCEPTMOE_ERR_NONFINITE = 1u << 2, /* a router logit is NaN or infinite                   */
-  ACCEPTMOE_ERR_COMMIT = 1u << 3     /* a commitment probability is negative or not finite  */
+  ACCEPTMOE_ERR_COMMIT = 1u << 3,    /* a commitment probability is negative or not finite  */
+  ACCEPTMOE_ERR_WORKSPACE = 1u << 4  /* an arrival counter of the workspace was not zero at
+                                        the start of the call (not zero-filled before its
+                                        first use, or shared by calls that overlap); the
+                                        counters are zero again afterwards                 */
 };
 
 /* Problem description; passed by HOST pointer and read during the call. */
@@ -147,7 +151,14 @@ typedef struct acceptmoe_stats {
  *             use (hipMemset at allocation); every call leaves the counters
  *             at zero again, so it needs no clearing between calls, also when
  *             the shape changes.  Calls that share a workspace must not
- *             overlap in time (same stream, or synchronised).
+ *             overlap in time (same stream, or synchronised).  A call that
+ *             finds a counter not at zero (a workspace not zero-filled, or
+ *             shared by overlapping calls) sets ACCEPTMOE_ERR_WORKSPACE in
+ *             stats->err_flags -- its other outputs are then unspecified, with
+ *             every index in range -- and sets the counters back to zero, so
+ *             the next call on that workspace is valid again.
+ *   stats->n_active / n_active_nonresident: U and the non-resident part of
+ *             it, counted from the restricted top-k (no grouping needed).
  * ------------------------------------------------------------------------- */
 size_t acceptmoe_select_workspace_size(const acceptmoe_shape* shape);
 int acceptmoe_select(const acceptmoe_shape* shape, const void* x, const void* w_router,

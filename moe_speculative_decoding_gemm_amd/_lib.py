@@ -24,7 +24,7 @@ F32, BF16, FP8_E4M3FN = 0, 1, 2
 F_NATURAL, F_NO_RENORM, F_LOGITS_IN = 1, 2, 4
 F_DEMAND_FULL, F_NO_ANCHOR, F_UNIT_COMMIT = 8, 16, 32
 LAYOUT_ROWMAJOR, LAYOUT_PACKED = 0, 1
-ERR_BAD_TREE, ERR_DEPTH, ERR_NONFINITE, ERR_COMMIT = 1, 2, 4, 8
+ERR_BAD_TREE, ERR_DEPTH, ERR_NONFINITE, ERR_COMMIT, ERR_WORKSPACE = 1, 2, 4, 8, 16
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3FN,
        torch.float8_e4m3fn: FP8_E4M3FN}
@@ -121,7 +121,8 @@ _lib = _load()
 EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "acceptmoe_packed_size", "acceptmoe_pack_experts",
-            "acceptmoe_workspace_size", "verify_block", "acceptmoe_cache_plan",
+            "acceptmoe_workspace_size", "verify_block",
+            "acceptmoe_cache_plan",
             "verify_block_cached", "acceptmoe_set_stage_timer",
             "acceptmoe_strerror",
             "acceptmoe_last_error", "acceptmoe_version")

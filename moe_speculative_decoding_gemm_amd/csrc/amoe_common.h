@@ -22,6 +22,7 @@ constexpr int kErrBadTree = 1;
 constexpr int kErrDepth = 2;
 constexpr int kErrNonFinite = 4;
 constexpr int kErrCommit = 8;
+constexpr int kErrWorkspace = 16;  // an arrival counter was not zero at the start of a call
 
 constexpr uint32_t kFlagNatural = 1u;
 constexpr uint32_t kFlagNoRenorm = 2u;
@@ -211,8 +212,11 @@ __device__ __forceinline__ float load_dev(const float* p) {
 // others wrote.  Each wave waits until its device-scope stores are complete
 // before the barrier; one thread then counts the arrival with an atomic
 // whose returned value decides.  The counter must be zero before the first
-// arrival; the last arriver resets it.
-__device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks) {
+// arrival; the last arriver resets it.  A count outside [0, nblocks) means
+// the counter did not start at zero (a workspace that was not zero-filled,
+// or shared by calls that overlap): kErrWorkspace is then OR-ed into
+// *misuse, and the caller's kernels still only read and write in range.
+__device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks, int* misuse) {
   __shared__ int s_last_dev;
   wait_global_stores();
   __syncthreads();
@@ -220,6 +224,8 @@ __device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks) {
     const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev == nblocks - 1;
     if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev < 0 || prev >= nblocks)
+      __hip_atomic_fetch_or(misuse, kErrWorkspace, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last_dev = last ? 1 : 0;
   }
   __syncthreads();
@@ -236,8 +242,9 @@ __device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks) {
 // second barrier.  One device-scope fence per work-group, not one per wave:
 // each such fence writes back the L2 of its XCD, and many of them in flight
 // serialise.  The counter must be zero before the first arrival; the last
-// work-group resets it, so it stays zero between launches.
-__device__ __forceinline__ bool last_block_done(int* counter, int nblocks) {
+// work-group resets it, so it stays zero between launches.  A count outside
+// [0, nblocks) is OR-ed into *misuse as kErrWorkspace (see last_arrival_dev).
+__device__ __forceinline__ bool last_block_done(int* counter, int nblocks, int* misuse) {
   __shared__ int s_last;
   wait_global_stores();
   __syncthreads();
@@ -250,6 +257,7 @@ __device__ __forceinline__ bool last_block_done(int* counter, int nblocks) {
       __threadfence();
       *counter = 0;  // ready for the next use
     }
+    if (prev < 0 || prev >= nblocks) atomicOr(misuse, kErrWorkspace);
     s_last = last ? 1 : 0;
   }
   __syncthreads();

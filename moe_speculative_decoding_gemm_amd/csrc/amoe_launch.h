@@ -7,6 +7,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// the C ABI's structs (include/acceptmoe.h)
+struct acceptmoe_shape;
+struct acceptmoe_inputs;
+struct acceptmoe_outputs;
+
 namespace amoe {
 
 struct SelectArgs {
@@ -38,7 +43,7 @@ struct SelectArgs {
   double* d_part;      // [E][groups, padded] demand summed over each 4-node group
   uint8_t* f_part;     // [E][groups, padded] bit 0: a root routes to the expert, bit 1: some node does
   int32_t* e_part;     // [groups] error bits of each node group
-  int32_t* counters;   // [2]: [1] restricted-kernel arrivals ([0] unused)
+  int32_t* counters;   // [2]: [0] arrivals seen outside their range, [1] restricted-kernel arrivals
   int32_t* gcount;     // [N/4]: K-slice arrivals per node group (zero between calls)
   // when non-null, the restricted top-k is followed by the grouping of the
   // assignments by expert (moe_route_permute's outputs)
@@ -130,5 +135,16 @@ hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm
 // active {0}, n_active {1}
 hipError_t launch_shared_grouping(int N, int32_t* offsets, int32_t* sorted_assign,
                                   int32_t* active, int32_t* n_active, hipStream_t stream);
+
+// Host helpers of capi.cpp for other entry points of the library.
+// check_verify_args: verify_block's argument checks (return code as the C
+// ABI's, detail in acceptmoe_last_error) and the workspace bytes it needs.
+// workspace_counter_bytes: the leading bytes of every workspace that hold
+// the kernels' arrival counters (zero between calls).  set_error: record a
+// detail string, return `code`.
+int check_verify_args(const ::acceptmoe_shape* s, const ::acceptmoe_inputs* in,
+                      const ::acceptmoe_outputs* out, size_t* need);
+size_t workspace_counter_bytes();
+int set_error(int code, const char* msg);
 
 }  // namespace amoe

@@ -254,6 +254,19 @@ int check_state(const acceptmoe_cache_state* st) {
     if (e < -1 || e >= st->E || (e >= 0 && (st->expert_slot[e] != q || !st->resident[e])))
       return fail(ACCEPTMOE_EINVAL, "cache state: slot %d holds expert %d inconsistently", q, e);
   }
+  // the other direction: a resident expert names a persistent slot that
+  // holds it; a non-resident expert names no persistent slot (a spill slot
+  // from the last block, n_slots .. n_slots + n_spill - 1, or -1)
+  for (int e = 0; e < st->E; ++e) {
+    const int q = st->expert_slot[e];
+    if (st->resident[e]) {
+      if (q < 0 || q >= st->n_slots || st->slot_expert[q] != e)
+        return fail(ACCEPTMOE_EINVAL, "cache state: resident expert %d names slot %d, which "
+                    "does not hold it", e, q);
+    } else if (q < -1 || (q >= 0 && q < st->n_slots) || q >= st->n_slots + st->n_spill) {
+      return fail(ACCEPTMOE_EINVAL, "cache state: non-resident expert %d names slot %d", e, q);
+    }
+  }
   return ACCEPTMOE_OK;
 }
 
@@ -425,6 +438,212 @@ int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const
   st->h2d_bytes += rep.h2d_bytes;
   if (report) *report = rep;
   return ACCEPTMOE_OK;
+}
+
+// Argument checks of verify_block / verify_block_cached, apart from the
+// workspace pointer: returns the workspace bytes the call needs in *need.
+int check_block_args(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                     const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
+                     size_t* need) {
+  int rc = check_shape(s, true);
+  if (rc) return rc;
+  if (!in || !out) return fail(ACCEPTMOE_EINVAL, "inputs or outputs is NULL");
+  const bool lin = (s->flags & ACCEPTMOE_F_LOGITS_IN) != 0;
+  if (lin ? !in->logits_in : (!in->x || !in->w_router))
+    return fail(ACCEPTMOE_EINVAL, lin ? "logits_in is NULL" : "x or w_router is NULL");
+  if (!in->x || !in->parent || !in->depth || !in->commit || !out->y)
+    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  if (!cache && (!in->w13 || !in->w2)) return fail(ACCEPTMOE_EINVAL, "w13 or w2 is NULL");
+  if (cache) {
+    rc = check_cache(s, cache);
+    if (rc) return rc;
+  }
+  const bool fp8 = s->w_dtype == ACCEPTMOE_FP8_E4M3FN;
+  if (fp8 && (!in->s13 || !in->s2)) return fail(ACCEPTMOE_EINVAL, "FP8 weights need s13 and s2");
+  const bool shared = in->w13_shared != nullptr;
+  if (shared && (!in->w2_shared || (fp8 && (!in->s13_shared || !in->s2_shared))))
+    return fail(ACCEPTMOE_EINVAL, "incomplete shared-expert weights");
+  Carver c(nullptr);
+  carve_verify(c, s, true);
+  *need = c.used;
+  return ACCEPTMOE_OK;
+}
+
+}  // namespace
+
+namespace amoe {
+
+int check_verify_args(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                      const acceptmoe_outputs* out, size_t* need) {
+  return check_block_args(s, in, nullptr, out, need);
+}
+
+size_t workspace_counter_bytes() {
+  // the arrival counters are the first two allocations of every workspace
+  Carver c(nullptr);
+  c.take<int32_t>(2);
+  c.take<int32_t>(4096 / 4);
+  return c.used;
+}
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+}  // namespace amoe
+
+namespace {
+
+// verify_block, and with `cache` set verify_block_cached: the expert weights
+// then come from the cache's device slots, after the missing ones are copied
+// in (one stream synchronization after the selection)
+int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+              const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
+              acceptmoe_cache_report* report, void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int rc = check_block_args(s, in, cache, out, &need);
+  if (rc) return rc;
+  if (!ws) return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
+  if (ws_bytes < need)
+    return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
+  const bool shared = in->w13_shared != nullptr;
+
+  Carver c(ws);
+  const VerifyWs w = carve_verify(c, s, shared);
+  uint8_t* eligible = out->eligible ? out->eligible : w.eligible;
+  int32_t* topk_idx = out->topk_idx ? out->topk_idx : w.topk_idx;
+  float* topk_gate = out->topk_gate ? out->topk_gate : w.topk_gate;
+  int32_t* counts = out->counts ? out->counts : w.counts;
+  int32_t* active = out->active ? out->active : w.active;
+  acceptmoe_stats* stats = out->stats ? out->stats : w.stats;
+
+  amoe::SelectArgs a = select_args(s, w.sel);
+  a.x = in->x;
+  a.w_router = in->w_router;
+  a.b_router = in->b_router;
+  a.logits_in = in->logits_in;
+  a.parent = in->parent;
+  a.depth = in->depth;
+  a.commit = in->commit;
+  a.resident = cache ? cache->dev_resident : in->resident;
+  a.logits_out = out->logits_out;
+  a.eligible = eligible;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.stats = stats;
+  // the selection stage also groups the assignments by expert
+  a.counts = counts;
+  a.offsets = w.offsets;
+  a.sorted_assign = w.sorted_assign;
+  a.inv_pos = w.inv_pos;
+  a.active = active;
+  a.n_active = w.n_active;
+  a.max_rows = w.n_active + 1;
+  a.groups = w.groups;
+  a.active_w = w.active_w;
+  timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
+  rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
+  bool overlap = false;
+  if (cache) {
+    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
+    if (rc) return rc;
+  }
+  amoe::GroupedArgs g;
+  g.N = s->N;
+  g.k = s->k;
+  g.E = s->E;
+  g.H = s->H;
+  g.I = s->I;
+  g.w_kind = w_kind(s->w_dtype);
+  g.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
+  g.x = in->x;
+  g.w13 = cache ? cache->dev_w13 : in->w13;
+  g.w2 = cache ? cache->dev_w2 : in->w2;
+  g.s13 = in->s13;
+  g.s2 = in->s2;
+  g.offsets = w.offsets;
+  g.sorted_assign = w.sorted_assign;
+  // the expert kernels take the active experts most-routed first: the work
+  // items of the few experts with many rows (the longest ones) then start on
+  // separate CUs, and the lightest items are the ones that share a CU last
+  g.active = w.active_w;
+  g.snake = 1;
+  g.n_active = w.n_active;
+  g.y_perm = w.y_perm;
+  g.h_perm = w.h_perm;
+  g.num_cu = num_cu();
+  g.packed = s->w_layout == ACCEPTMOE_LAYOUT_PACKED;
+  // bf16 / fp8 weights: the down projection writes token-major rows, so the
+  // combine gathers without inv_pos (same values, same arithmetic)
+  g.tok_rows = g.w_kind != 0;
+  g.row_groups = 1;
+  g.max_rows = w.n_active + 1;
+  g.groups = w.groups;
+  g.w_slot = cache ? cache->dev_expert_slot : nullptr;
+  g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
+  timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
+  if (overlap) {
+    // the hit experts while the missing ones are copied in, then those (the
+    // row-group table indexes the full active list: not used for the two lists)
+    const int32_t* lists = cache->dev_lists;
+    g.groups = nullptr;
+    g.snake = 0;
+    g.active = lists;
+    g.n_active = lists + s->E;
+    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");
+    if (rc) return rc;
+    rc = hip_status(hipStreamWaitEvent(stream, cache->copy_done, 0), "verify_block_cached/wait");
+    if (rc) return rc;
+    g.active = lists + s->E + 1;
+    g.n_active = lists + 2 * s->E + 1;
+    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched experts");
+    if (rc) return rc;
+  } else {
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
+    rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
+    timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
+    rc = hip_status(amoe::launch_grouped(g, stream, 2), "verify_block/experts down");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
+  }
+  timer_mark(ACCEPTMOE_STAGE_EXPERTS, false, stream);
+  timer_mark(ACCEPTMOE_STAGE_COMBINE, true, stream);
+  if (shared) {
+    rc = hip_status(amoe::launch_shared_grouping(s->N, w.sh_offsets, w.sh_sorted, w.sh_active,
+                                                 w.sh_n_active, stream),
+                    "verify_block/shared grouping");
+    if (rc) return rc;
+    amoe::GroupedArgs gs = g;
+    gs.k = 1;
+    gs.E = 1;
+    gs.w13 = in->w13_shared;
+    gs.w2 = in->w2_shared;
+    gs.s13 = in->s13_shared;
+    gs.s2 = in->s2_shared;
+    gs.offsets = w.sh_offsets;
+    gs.sorted_assign = w.sh_sorted;
+    gs.active = w.sh_active;
+    gs.n_active = w.sh_n_active;
+    gs.y_perm = w.sh_y;
+    gs.h_perm = w.sh_h;
+    gs.tok_rows = 0;
+    gs.w_slot = nullptr;
+    gs.max_rows = nullptr;
+    gs.groups = nullptr;
+    gs.snake = 0;
+    gs.n_wslots = 0;
+    gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
+    rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
+    if (rc) return rc;
+  }
+  rc = hip_status(amoe::launch_combine(s->N, s->k, s->H, s->act_dtype == ACCEPTMOE_BF16,
+                                       w.y_perm, g.tok_rows ? nullptr : w.inv_pos, topk_gate,
+                                       shared ? w.sh_y : nullptr, out->y, stream),
+                  "verify_block/combine");
+  timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);
+  return rc;
 }
 
 }  // namespace
@@ -626,175 +845,6 @@ size_t acceptmoe_workspace_size(const acceptmoe_shape* s) {
   Carver c(nullptr);
   carve_verify(c, s, true);
   return c.used;
-}
-
-// verify_block, and with `cache` set verify_block_cached: the expert weights
-// then come from the cache's device slots, after the missing ones are copied
-// in (one stream synchronization after the selection)
-static int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
-                     const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
-                     acceptmoe_cache_report* report, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
-  int rc = check_shape(s, true);
-  if (rc) return rc;
-  if (!in || !out) return fail(ACCEPTMOE_EINVAL, "inputs or outputs is NULL");
-  const bool lin = (s->flags & ACCEPTMOE_F_LOGITS_IN) != 0;
-  if (lin ? !in->logits_in : (!in->x || !in->w_router))
-    return fail(ACCEPTMOE_EINVAL, lin ? "logits_in is NULL" : "x or w_router is NULL");
-  if (!in->x || !in->parent || !in->depth || !in->commit || !out->y || !ws)
-    return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
-  if (!cache && (!in->w13 || !in->w2)) return fail(ACCEPTMOE_EINVAL, "w13 or w2 is NULL");
-  if (cache) {
-    rc = check_cache(s, cache);
-    if (rc) return rc;
-  }
-  const bool fp8 = s->w_dtype == ACCEPTMOE_FP8_E4M3FN;
-  if (fp8 && (!in->s13 || !in->s2)) return fail(ACCEPTMOE_EINVAL, "FP8 weights need s13 and s2");
-  const bool shared = in->w13_shared != nullptr;
-  if (shared && (!in->w2_shared || (fp8 && (!in->s13_shared || !in->s2_shared))))
-    return fail(ACCEPTMOE_EINVAL, "incomplete shared-expert weights");
-  const size_t need = acceptmoe_workspace_size(s);
-  if (ws_bytes < need)
-    return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
-
-  Carver c(ws);
-  const VerifyWs w = carve_verify(c, s, shared);
-  uint8_t* eligible = out->eligible ? out->eligible : w.eligible;
-  int32_t* topk_idx = out->topk_idx ? out->topk_idx : w.topk_idx;
-  float* topk_gate = out->topk_gate ? out->topk_gate : w.topk_gate;
-  int32_t* counts = out->counts ? out->counts : w.counts;
-  int32_t* active = out->active ? out->active : w.active;
-  acceptmoe_stats* stats = out->stats ? out->stats : w.stats;
-
-  amoe::SelectArgs a = select_args(s, w.sel);
-  a.x = in->x;
-  a.w_router = in->w_router;
-  a.b_router = in->b_router;
-  a.logits_in = in->logits_in;
-  a.parent = in->parent;
-  a.depth = in->depth;
-  a.commit = in->commit;
-  a.resident = cache ? cache->dev_resident : in->resident;
-  a.logits_out = out->logits_out;
-  a.eligible = eligible;
-  a.topk_idx = topk_idx;
-  a.topk_gate = topk_gate;
-  a.stats = stats;
-  // the selection stage also groups the assignments by expert
-  a.counts = counts;
-  a.offsets = w.offsets;
-  a.sorted_assign = w.sorted_assign;
-  a.inv_pos = w.inv_pos;
-  a.active = active;
-  a.n_active = w.n_active;
-  a.max_rows = w.n_active + 1;
-  a.groups = w.groups;
-  a.active_w = w.active_w;
-  timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
-  rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
-  if (rc) return rc;
-  timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
-  bool overlap = false;
-  if (cache) {
-    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
-    if (rc) return rc;
-  }
-  amoe::GroupedArgs g;
-  g.N = s->N;
-  g.k = s->k;
-  g.E = s->E;
-  g.H = s->H;
-  g.I = s->I;
-  g.w_kind = w_kind(s->w_dtype);
-  g.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
-  g.x = in->x;
-  g.w13 = cache ? cache->dev_w13 : in->w13;
-  g.w2 = cache ? cache->dev_w2 : in->w2;
-  g.s13 = in->s13;
-  g.s2 = in->s2;
-  g.offsets = w.offsets;
-  g.sorted_assign = w.sorted_assign;
-  // the expert kernels take the active experts most-routed first: the work
-  // items of the few experts with many rows (the longest ones) then start on
-  // separate CUs, and the lightest items are the ones that share a CU last
-  g.active = w.active_w;
-  g.snake = 1;
-  g.n_active = w.n_active;
-  g.y_perm = w.y_perm;
-  g.h_perm = w.h_perm;
-  g.num_cu = num_cu();
-  g.packed = s->w_layout == ACCEPTMOE_LAYOUT_PACKED;
-  // bf16 / fp8 weights: the down projection writes token-major rows, so the
-  // combine gathers without inv_pos (same values, same arithmetic)
-  g.tok_rows = g.w_kind != 0;
-  g.row_groups = 1;
-  g.max_rows = w.n_active + 1;
-  g.groups = w.groups;
-  g.w_slot = cache ? cache->dev_expert_slot : nullptr;
-  g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
-  timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
-  if (overlap) {
-    // the hit experts while the missing ones are copied in, then those (the
-    // row-group table indexes the full active list: not used for the two lists)
-    const int32_t* lists = cache->dev_lists;
-    g.groups = nullptr;
-    g.snake = 0;
-    g.active = lists;
-    g.n_active = lists + s->E;
-    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");
-    if (rc) return rc;
-    rc = hip_status(hipStreamWaitEvent(stream, cache->copy_done, 0), "verify_block_cached/wait");
-    if (rc) return rc;
-    g.active = lists + s->E + 1;
-    g.n_active = lists + 2 * s->E + 1;
-    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched experts");
-    if (rc) return rc;
-  } else {
-    timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
-    rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
-    if (rc) return rc;
-    timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
-    timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
-    rc = hip_status(amoe::launch_grouped(g, stream, 2), "verify_block/experts down");
-    if (rc) return rc;
-    timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
-  }
-  timer_mark(ACCEPTMOE_STAGE_EXPERTS, false, stream);
-  timer_mark(ACCEPTMOE_STAGE_COMBINE, true, stream);
-  if (shared) {
-    rc = hip_status(amoe::launch_shared_grouping(s->N, w.sh_offsets, w.sh_sorted, w.sh_active,
-                                                 w.sh_n_active, stream),
-                    "verify_block/shared grouping");
-    if (rc) return rc;
-    amoe::GroupedArgs gs = g;
-    gs.k = 1;
-    gs.E = 1;
-    gs.w13 = in->w13_shared;
-    gs.w2 = in->w2_shared;
-    gs.s13 = in->s13_shared;
-    gs.s2 = in->s2_shared;
-    gs.offsets = w.sh_offsets;
-    gs.sorted_assign = w.sh_sorted;
-    gs.active = w.sh_active;
-    gs.n_active = w.sh_n_active;
-    gs.y_perm = w.sh_y;
-    gs.h_perm = w.sh_h;
-    gs.tok_rows = 0;
-    gs.w_slot = nullptr;
-    gs.max_rows = nullptr;
-    gs.groups = nullptr;
-    gs.snake = 0;
-    gs.n_wslots = 0;
-    gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
-    rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
-    if (rc) return rc;
-  }
-  rc = hip_status(amoe::launch_combine(s->N, s->k, s->H, s->act_dtype == ACCEPTMOE_BF16,
-                                       w.y_perm, g.tok_rows ? nullptr : w.inv_pos, topk_gate,
-                                       shared ? w.sh_y : nullptr, out->y, stream),
-                  "verify_block/combine");
-  timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);
-  return rc;
 }
 
 int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,

@@ -337,10 +337,11 @@ __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E
 }
 
 // One kTail-thread work-group.  nwg partial rows (per expert, expert-major)
-// of demand / flags, nwg error words.  Leaves the eligible flags in sm.elig
-// (and in a.eligible), statistics in a.stats (n_active is filled by the
-// grouping).
-__device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
+// of demand / flags, nwg error words; ws_err: error bits found by the
+// workspace check (OR-ed in by any thread).  Leaves the eligible flags in
+// sm.elig (and in a.eligible), statistics in a.stats (n_active and
+// n_active_nonresident follow once the restricted top-k is known).
+__device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm, int ws_err) {
   static_assert(kMaxE == 256 && kTail >= kMaxE, "select_set keeps one thread per expert slot");
   const int t = threadIdx.x;
   const int E = a.E, k = a.k;
@@ -396,7 +397,7 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     sm.key[t] = in_fill ? dsum : -1.0;
     sm.elig[t] = in_fill;
   }
-  if (err0) atomicOr(&sm.err, err0);
+  if (err0 | ws_err) atomicOr(&sm.err, err0 | ws_err);
   for (int w = t + kTail; w < nwg; w += kTail) {
     const int e = a.e_part[w];
     if (e) atomicOr(&sm.err, e);
@@ -473,6 +474,33 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm) {
     st->err_flags = sm.err;
     st->r_eff = r_eff;
     st->demand_total = tot;
+  }
+}
+
+// U (unique experts of the restricted top-k) and how many of them are not
+// resident, from the N*k chosen experts (LDS or global), by the whole
+// work-group when no grouping follows; flag: kMaxE ints of scratch.  The
+// grouping (permute_block) writes the same two statistics itself.
+template <int NTHR>
+__device__ __forceinline__ void active_stats(int NK, int E, const int32_t* sel,
+                                             const uint8_t* resident, StatsDev* st, int* flag) {
+  const int t = threadIdx.x;
+  if (t < kMaxE) flag[t] = 0;
+  __syncthreads();
+  for (int x = t; x < NK; x += NTHR) flag[clamp_expert(sel[x], E)] = 1;
+  __syncthreads();
+  if (t < kWave) {
+    int na = 0, nr = 0;
+    for (int e = t; e < E; e += kWave) {
+      na += flag[e];
+      nr += (flag[e] && resident && !resident[e]) ? 1 : 0;
+    }
+    na = static_cast<int>(readlane_u32(wave_inclusive_sum_u32(static_cast<uint32_t>(na)), kWave - 1));
+    nr = static_cast<int>(readlane_u32(wave_inclusive_sum_u32(static_cast<uint32_t>(nr)), kWave - 1));
+    if (t == 0) {
+      st->n_active = na;
+      st->n_active_nonresident = nr;
+    }
   }
 }
 
@@ -654,6 +682,9 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
     permute_block<kTail>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
                        a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
                        sm.u.perm, a.max_rows, a.groups, a.active_w);
+  else
+    active_stats<kTail>(NK, E, sm.top_e, a.resident, static_cast<StatsDev*>(a.stats),
+                        sm.set.rank);
 }
 
 // commit[depth] and the parent's depth of node `node` (of any wave: clamped
@@ -771,7 +802,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
     else
       router_partials<AT, 4>(a, g, ks, wave, lane, node, d, p, cf, dp);
     // partials travel at device scope: no cache write-back or invalidation
-    if (!last_arrival_dev(&a.gcount[g], gridDim.y)) return;
+    if (!last_arrival_dev(&a.gcount[g], gridDim.y, &a.counters[0])) return;
   } else {
     node_deps(a, node, d, p, cf, dp);
   }
@@ -800,14 +831,35 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
 // The set selection and, for N <= kFusedMaxN, every node's restricted top-k,
 // the gates and the grouping: one work-group of kTail threads, after the
 // front kernel.  The node phase's outputs are loaded first, all together.
+// Every arrival counter of the workspace must be zero between kernels of a
+// call: the front kernel's elections leave its group counters at zero and
+// note any count outside its range in counters[0].  A nonzero counter here
+// means the workspace was not zero-filled before its first use, or was
+// shared by calls that overlap: the call's outputs are then flagged
+// (kErrWorkspace), and the counters are set back to zero so that the
+// restricted kernel of this call and later calls elect correctly.  Runs
+// before the tail kernel's first barrier; returns the error bits.
+__device__ __forceinline__ int check_counters(const SelectArgs& a, int nwg) {
+  int bad = 0;
+  for (int g = static_cast<int>(threadIdx.x); g < nwg + 2; g += kTail) {
+    int* c = g < nwg ? &a.gcount[g] : &a.counters[g - nwg];
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+      bad = kErrWorkspace;
+      __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return bad;
+}
+
 __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) TailSmem sm;
   const int t = threadIdx.x;
   const int N = a.N, E = a.E;
   const int nwg = node_groups(N);
   const bool fused = N <= kFusedMaxN;
+  const int ws_err = check_counters(a, nwg);
   if (!fused) {
-    select_set(a, nwg, sm.set);
+    select_set(a, nwg, sm.set, ws_err);
     return;
   }
   // natural top-k, its logits, max / sum of exp per node, and (when they
@@ -836,7 +888,7 @@ __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
     pm = a.node_m[t];
     pz = a.node_z[t];
   }
-  select_set(a, nwg, sm.set);
+  select_set(a, nwg, sm.set, ws_err);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (x4 + j < NK) {
@@ -923,11 +975,16 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
       a.topk_gate[static_cast<size_t>(i) * k + lane] = static_cast<float>(g);
     }
   }
-  if (a.counts) {
-    if (last_block_done(&a.counters[1], gridDim.x))
+  // the last work-group to finish groups the assignments by expert, or
+  // (without the grouping) counts the active experts for the statistics
+  StatsDev* st = static_cast<StatsDev*>(a.stats);
+  if (last_block_done(&a.counters[1], gridDim.x, &st->err_flags)) {
+    if (a.counts)
       permute_block<256>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
-                         a.inv_pos, a.active, a.n_active, a.resident,
-                         static_cast<StatsDev*>(a.stats), perm, a.max_rows, a.groups, a.active_w);
+                         a.inv_pos, a.active, a.n_active, a.resident, st, perm, a.max_rows,
+                         a.groups, a.active_w);
+    else
+      active_stats<256>(a.N * a.k, a.E, a.topk_idx, a.resident, st, perm.cnt);
   }
 }
 

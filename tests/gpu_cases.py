@@ -50,23 +50,70 @@ def make_weights(cfg, device="cuda", layer=0, gen_device=None):
     return out
 
 
-def expert_fn_from(cfg, w):
-    """Oracle accessor reading one expert's exact weights back from the device."""
+def _exact_expert(cfg, w, e):
+    """One expert's exact fp64 (Wg, Wu, Wd), read back from the device."""
+    if cfg.w == "fp8":
+        q13 = w["w13"][e].cpu().numpy()
+        s13 = w["s13"][e].cpu().numpy()
+        return (OF8.dequant_blocks(q13[0], s13[0]), OF8.dequant_blocks(q13[1], s13[1]),
+                OF8.dequant_blocks(w["w2"][e].cpu().numpy(), w["s2"][e].cpu().numpy()))
+    w13 = W.to_exact_f64(w["w13"][e])
+    return (w13[0], w13[1], W.to_exact_f64(w["w2"][e]))
+
+
+def expert_fn_from(cfg, w, cache_size=48):
+    """Oracle accessor reading one expert's exact weights back from the device
+    (the last `cache_size` distinct experts are kept)."""
     cache = {}
 
     def fn(e):
         if e in cache:
             return cache[e]
-        if cfg.w == "fp8":
-            q13 = w["w13"][e].cpu().numpy()
-            s13 = w["s13"][e].cpu().numpy()
-            val = (OF8.dequant_blocks(q13[0], s13[0]), OF8.dequant_blocks(q13[1], s13[1]),
-                   OF8.dequant_blocks(w["w2"][e].cpu().numpy(), w["s2"][e].cpu().numpy()))
-        else:
-            w13 = W.to_exact_f64(w["w13"][e])
-            val = (w13[0], w13[1], W.to_exact_f64(w["w2"][e]))
-        if len(cache) < 48:
+        val = _exact_expert(cfg, w, e)
+        if len(cache) < cache_size:
             cache[e] = val
+        return val
+    return fn
+
+
+def expert_fn_streaming(cfg, w, order, threads=8, window=12):
+    """Oracle accessor for experts requested once each in `order` (the
+    grouped layer's ascending active list): the exact weights of the next
+    `window` experts are prepared by a thread pool ahead of the request, and
+    dropped once handed out, so a full-size layer costs little host memory.
+    The device reads happen here, on the calling thread."""
+    import concurrent.futures as cf
+    order = [int(e) for e in order]
+    pos = {e: i for i, e in enumerate(order)}
+    ex = cf.ThreadPoolExecutor(max_workers=threads)
+    futs = {}
+
+    def submit(i):
+        if i < len(order) and order[i] not in futs:
+            e = order[i]
+            if cfg.w == "fp8":
+                raw = (w["w13"][e].cpu().numpy(), w["s13"][e].cpu().numpy(),
+                       w["w2"][e].cpu().numpy(), w["s2"][e].cpu().numpy())
+                futs[e] = ex.submit(lambda r: (OF8.dequant_blocks(r[0][0], r[1][0]),
+                                               OF8.dequant_blocks(r[0][1], r[1][1]),
+                                               OF8.dequant_blocks(r[2], r[3])), raw)
+            else:
+                raw = (w["w13"][e].cpu(), w["w2"][e].cpu())
+                futs[e] = ex.submit(lambda r: (W.to_exact_f64(r[0][0]), W.to_exact_f64(r[0][1]),
+                                               W.to_exact_f64(r[1])), raw)
+
+    for i in range(min(window, len(order))):
+        submit(i)
+
+    def fn(e):
+        e = int(e)
+        if e not in pos:
+            return _exact_expert(cfg, w, e)
+        submit(pos[e])
+        val = futs.pop(e).result()
+        submit(pos[e] + window)
+        if pos[e] == len(order) - 1:
+            ex.shutdown(wait=False)
         return val
     return fn
 
@@ -111,7 +158,8 @@ def check_selection(gpu: dict, ref: dict, stats: dict, cfg, ctx=""):
     rg = ref["topk_gate"].astype(np.float64)
     assert np.max(np.abs(tg - rg) / np.abs(rg)) <= 1e-6, f"{ctx}: gates differ"
     rs = ref["stats"]
-    for key in ("n_anchor", "n_selfsize", "n_eligible", "n_pruned", "n_natural_union"):
+    for key in ("n_anchor", "n_selfsize", "n_eligible", "n_pruned", "n_natural_union",
+                "n_active", "n_active_nonresident"):
         assert stats[key] == rs[key], f"{ctx}: stats {key} {stats[key]} != {rs[key]}"
     assert stats["err_flags"] == 0
     assert abs(stats["r_eff"] - rs["r_eff"]) <= 1e-12 * max(1.0, rs["r_eff"]), ctx

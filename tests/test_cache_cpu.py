@@ -128,6 +128,31 @@ def test_inconsistent_state_rejected(m):
     with pytest.raises(m.AcceptMoEError) as ei:
         c.plan([1])
     assert ei.value.code == m.EINVAL
+    # a warm start whose expert side disagrees with the slot table: the plan
+    # would otherwise count the expert as a hit and index last_use by its slot
+    for bad_slot in (-1, 7, 2):
+        c = make(m, 16, 4, 4)
+        c.reset([5, 6])
+        c.resident[9] = 1            # resident, but no slot holds expert 9
+        c.expert_slot[9] = bad_slot  # -1, a spill slot, or slot 2 (empty)
+        before = (c.slot_expert.clone(), c.expert_slot.clone(), c.resident.clone())
+        with pytest.raises(m.AcceptMoEError) as ei:
+            c.plan([9])
+        assert ei.value.code == m.EINVAL
+        assert all(a.equal(b) for a, b in zip(before, (c.slot_expert, c.expert_slot,
+                                                        c.resident)))
+    # a non-resident expert that names a persistent slot
+    c = make(m, 16, 4, 4)
+    c.reset([5, 6])
+    c.expert_slot[2] = 1
+    with pytest.raises(m.AcceptMoEError) as ei:
+        c.plan([2])
+    assert ei.value.code == m.EINVAL
+    # a spill slot from the previous block is a valid state
+    c = make(m, 16, 1, 2)
+    c.plan([1, 2])                   # 2 spills into slot 1
+    assert int(c.expert_slot[2]) == 1 and int(c.resident[2]) == 0
+    assert c.plan([2]) == [(2, 0)]
 
 
 def test_cached_block_argument_checks(m):

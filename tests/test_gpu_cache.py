@@ -5,7 +5,8 @@ A sequence of seeded blocks runs through verify_block_cached on an expert
 cache of a few device slots.  Each block must give bit-identical outputs to
 verify_block on the fully resident weights with the cache's resident mask of
 that moment (the same kernels read the same weight bytes, only from slots),
-so its parity with the oracle is the parity of verify_block.  The copies must
+and match the oracle's layer with that mask: the selection bit-exact given
+the GPU's logits, y within the dtype's tolerance.  The copies must
 follow the oracle's LRU model exactly: the fetched experts, spills, hits and
 host-to-device bytes, and the device slot table must equal the host state.
 """
@@ -13,8 +14,10 @@ host-to-device bytes, and the device slot table must equal the host state.
 import pytest
 import torch
 
+import oracle as O
 import workloads as W
-from gpu_cases import make_weights, say, shape_of, upload_block
+from gpu_cases import (TOL, check_selection, expert_fn_from, make_weights, max_rel_err, say,
+                       shape_of, shared_fn_from, upload_block)
 from oracle.cache import LRUExpertCache
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +59,7 @@ def test_cached_block_matches_resident_block(lib, name, over, slots, spill, over
     model = LRUExpertCache(slots, spill, warm)
     per_expert = cache.b13 + cache.b2
     total = 0
+    fn, shfn = expert_fn_from(cfg, w), shared_fn_from(cfg, w)
     for seed in range(6):
         say(f"cache {name} {over} slots={slots} spill={spill} overlap={overlap} seed {seed}")
         b = W.make_block(cfg, seed)
@@ -68,6 +72,18 @@ def test_cached_block_matches_resident_block(lib, name, over, slots, spill, over
         for key in ("y", "logits_out", "eligible", "topk_idx", "topk_gate", "counts", "stats"):
             assert torch.equal(out[key], ref[key]), f"seed {seed}: {key} differs"
         st = lib.decode_stats(out["stats"])
+        # and against the oracle's layer with the cache's resident mask of
+        # that moment (selection bit-exact given the GPU's logits)
+        mask = res_before.cpu().numpy().astype(bool)
+        lg = out["logits_out"].cpu().numpy()
+        oref = O.verify_block(
+            k=cfg.k, x=W.to_exact_f64(b.x), expert_fn=fn, parent=b.parent, depth=b.depth,
+            commit=b.commit, logits_in=lg, resident=mask, min_set=cfg.min_set,
+            fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute, flags=cfg.flags,
+            shared_fn=shfn)
+        assert check_selection(out, oref, st, cfg, f"cached seed {seed}")
+        err = max_rel_err(out["y"], oref["y"])
+        assert err <= TOL[cfg.w], (seed, err)
         U = st["n_active"]
         assert torch.equal(out["active"][:U], ref["active"][:U])  # entries past U are unset
         active = out["active"][:U].cpu().tolist()

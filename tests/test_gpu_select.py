@@ -136,8 +136,9 @@ def test_logits_in_and_edge_shapes(lib):
         out, st = run_select(lib, cfg, b, flags=lib.F_LOGITS_IN, logits_in=lg)
         ref = oracle_select(cfg, b, logits_in=lg, flags=0)
         assert (out["logits_out"].cpu().numpy().view(np.uint32) == lg.view(np.uint32)).all()
-        if not ref["near_tie"]:
-            check_selection(out, ref, st, cfg, f"edge {c}")
+        # every case is compared: none of them may rest on an fp64 near tie
+        assert not ref["near_tie"], f"edge {c}: near tie, pick other inputs"
+        assert check_selection(out, ref, st, cfg, f"edge {c}")
 
 
 def test_device_error_flags(lib):
@@ -235,3 +236,52 @@ def test_selector_variants(lib, name, over, vname, flags, budget):
             assert st["n_anchor"] == 0
         if budget and not (flags & 16) and cfg.resident_slots == 0:
             assert st["n_eligible"] == max(budget, st["n_anchor"], cfg.k, cfg.min_set)
+
+
+@pytest.mark.parametrize("N", [40, 300], ids=["tail_topk", "restricted_kernel"])
+def test_workspace_misuse_is_flagged_and_repaired(lib, N):
+    """A workspace whose arrival counters are not zero (never zero-filled, or
+    shared by overlapping calls) must not go unnoticed: the call sets
+    ERR_WORKSPACE, keeps every index in range, and leaves the counters at
+    zero, so the next call on the same workspace is exact again.  Counters
+    set here: a node group's K-slice counter below its slice count (one
+    work-group is elected too early), another far above it (none is
+    elected), and the restricted kernel's counter."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=32, k=4, H=256, N=N)
+    b = W.make_block(cfg, 1)
+    d = upload_block(b)
+    sh = shape_of(lib, cfg)
+    dev = "cuda"
+    ws = torch.zeros(lib.acceptmoe_select_workspace_size(sh), dtype=torch.uint8, device=dev)
+
+    def call():
+        o = dict(logits_out=torch.empty((N, cfg.E), dtype=torch.float32, device=dev),
+                 eligible=torch.empty(cfg.E, dtype=torch.uint8, device=dev),
+                 topk_idx=torch.empty((N, cfg.k), dtype=torch.int32, device=dev),
+                 topk_gate=torch.empty((N, cfg.k), dtype=torch.float32, device=dev),
+                 stats=lib.new_stats(dev))
+        lib.acceptmoe_select(sh, d["x"], d["w_router"], d["b_router"], None, d["parent"],
+                             d["depth"], d["commit"], None, o["logits_out"], o["eligible"],
+                             o["topk_idx"], o["topk_gate"], o["stats"], ws)
+        torch.cuda.synchronize()
+        return o, lib.decode_stats(o["stats"])
+
+    ref, st0 = call()
+    assert st0["err_flags"] == 0
+    # workspace layout: counters[2] at byte 0, the node groups' K-slice
+    # counters from byte 256 (int index 64)
+    c = ws.view(torch.int32)
+    c[64 + 0] = 1          # group 0: elected after its first arrival
+    c[64 + 1] = 1000       # group 1: never elected
+    c[1] = 5               # restricted kernel's arrivals
+    torch.cuda.synchronize()
+    say(f"workspace misuse N={N}")
+    bad, st1 = call()
+    assert st1["err_flags"] & lib.ERR_WORKSPACE, st1
+    ti = bad["topk_idx"].cpu().numpy()
+    assert ((ti >= 0) & (ti < cfg.E)).all()
+    assert int(c[64]) == 0 and int(c[65]) == 0 and int(c[1]) == 0 and int(c[0]) == 0
+    good, st2 = call()
+    assert st2 == st0
+    for key in ref:
+        assert torch.equal(good[key], ref[key]), key

@@ -14,6 +14,7 @@ import os
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 import oracle as O
@@ -63,6 +64,50 @@ def test_blog_16x2_example_union_and_permute():
                  logits_in=L, flags=O.F_NATURAL)
     assert s["topk_idx"].tolist() == g["candidates"]
     assert s["stats"]["n_active"] == 5 and s["stats"]["reuse"] == pytest.approx(0.375)
+
+
+def test_blog_16x2_example_as_chain_end_to_end():
+    """The blog's 16-expert / top-2 example (dense vs MoE verification) run
+    as a draft chain with the tiny layer's commitment table [1, .7, .45, .3]:
+    every AcceptMoE step end to end (demand reading, effective rank,
+    round-half-up set size, anchor + fill order, restricted top-k with the
+    lower-index tie rule, gates, grouping).  The expected values are derived
+    here in closed form from the example's logits (2 for a candidate's first
+    expert, 1 for its second, 0 elsewhere), not taken from the oracle."""
+    g = _load("blog_16x2_example.json")
+    E, k = g["E"], g["k"]
+    cand = g["candidates"]                      # [[2,7],[2,7],[2,9],[4,11]]
+    L = _logits_for_sets(cand, E)
+    commit = [1.0, 0.7, 0.45, 0.3]
+    s = O.select(k=k, parent=[-1, 0, 1, 2], depth=[0, 1, 2, 3], commit=commit, logits_in=L)
+    # scores: exp(2), exp(1), 1 over the row's sum exp(2) + exp(1) + 14
+    zr = math.exp(2) + math.exp(1) + 14.0
+    p1, p2 = math.exp(2) / zr, math.exp(1) / zr
+    want_D = np.zeros(E)
+    for i, (a, b) in enumerate(cand):           # a node's demand: c * p of its own top-2
+        want_D[a] += commit[i] * p1
+        want_D[b] += commit[i] * p2
+    np.testing.assert_allclose(s["demand"], want_D, rtol=1e-14, atol=0)
+    assert want_D[2] == pytest.approx(2.15 * p1) and want_D[7] == pytest.approx(1.7 * p2)
+    r_eff = math.exp(scipy.stats.entropy(want_D[want_D > 0]))
+    assert s["r_eff"] == pytest.approx(r_eff, rel=1e-12)
+    assert 2.9 < r_eff < 3.0                    # rounds half up to 3
+    assert s["n"] == 3 and s["anchor"] == {2, 7}
+    # anchor {2, 7}, then the highest remaining demand: E4 (0.3 p1 > 0.45 p2)
+    assert sorted(np.nonzero(s["eligible"])[0].tolist()) == [2, 4, 7]
+    # node 2 keeps E2 and takes E4 over E7 (both logit 0: lower index);
+    # node 3 keeps E4 and takes E2 over E7 the same way
+    assert s["topk_idx"].tolist() == [[2, 7], [2, 7], [2, 4], [4, 2]]
+    e = math.e
+    want_g = [[e / (e + 1), 1 / (e + 1)]] * 2 + [[e * e / (e * e + 1), 1 / (e * e + 1)]] * 2
+    np.testing.assert_allclose(s["topk_gate"], np.array(want_g, np.float32), rtol=0, atol=0)
+    perm = O.permute(s["topk_idx"], E)
+    # assignments i*2+j -> experts [2,7,2,7,2,4,4,2]: stable grouping by expert
+    assert perm["sorted_assign"].tolist() == [0, 2, 4, 7, 5, 6, 1, 3]
+    assert perm["inv_pos"].tolist() == [0, 6, 1, 7, 2, 4, 5, 3]
+    assert {int(x): int(perm["counts"][x]) for x in perm["active"]} == {2: 4, 4: 2, 7: 2}
+    assert s["stats"]["n_active"] == 3 and s["stats"]["n_natural_union"] == 5
+    assert not s["near_tie"]
 
 
 def test_blog_tree_example_union():
