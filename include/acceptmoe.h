@@ -289,6 +289,30 @@ int verify_block(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
                  const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * verify_block_noalloc -- verify_block for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that never call hipMalloc): the workspace is the library's own device
+ * array of ACCEPTMOE_NOALLOC_WORKSPACE_BYTES (one per GPU the library runs
+ * on, held until the process ends), so the call takes no ws argument and
+ * allocates nothing.  Inputs and outputs are the caller's, as for
+ * verify_block, and the results are the same.
+ *   Errors: as verify_block; a shape whose workspace
+ *   (acceptmoe_workspace_size) exceeds ACCEPTMOE_NOALLOC_WORKSPACE_BYTES is
+ *   rejected with ACCEPTMOE_EINVAL before anything is enqueued (every
+ *   64-node block of hidden size <= 4096 fits; the 256-node DeepSeek-shaped
+ *   block does not).  ACCEPTMOE_EHIP if the array's device address cannot be
+ *   looked up.
+ *   Each call clears the array's arrival counters on `stream` first (a
+ *   kernel, so the call can be captured in a graph).  Every call on one GPU
+ *   shares that GPU's array and leaves the last call's contents in it: calls
+ *   that overlap in time on one GPU race -- serialise them (one stream, or
+ *   events).
+ * ------------------------------------------------------------------------- */
+#define ACCEPTMOE_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+int verify_block_noalloc(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
+                         const acceptmoe_outputs* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Profiling aid: per-thread stage timer.  After
  * acceptmoe_set_stage_timer(stage, start, stop), every later verify_block call
  * on this host thread records `start` on its stream right before the first

@@ -103,6 +103,7 @@ def _load():
         "moe_combine": (C.c_int, [i32] * 4 + [vp] * 5 + [vp]),
         "acceptmoe_workspace_size": (sz, [vp]),
         "verify_block": (C.c_int, [vp, vp, vp, vp, sz, vp]),
+        "verify_block_noalloc": (C.c_int, [vp, vp, vp, vp]),
         "acceptmoe_cache_plan": (C.c_int, [vp, vp, i32, vp, vp, vp]),
         "verify_block_cached": (C.c_int, [vp, vp, vp, vp, vp, vp, sz, vp]),
         "acceptmoe_set_stage_timer": (C.c_int, [i32, vp, vp]),
@@ -121,7 +122,7 @@ _lib = _load()
 EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "acceptmoe_packed_size", "acceptmoe_pack_experts",
-            "acceptmoe_workspace_size", "verify_block",
+            "acceptmoe_workspace_size", "verify_block", "verify_block_noalloc",
             "acceptmoe_cache_plan",
             "verify_block_cached", "acceptmoe_set_stage_timer",
             "acceptmoe_strerror",
@@ -359,6 +360,17 @@ def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
     _check(_lib.verify_block(C.byref(shape), C.byref(inp), C.byref(out),
                              _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0,
                              _stream(stream)), "verify_block")
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20  # the library's own workspace of verify_block_noalloc
+
+
+def verify_block_noalloc(shape: Shape, inputs: dict, outputs: dict, stream=None):
+    """verify_block with the library's own device workspace (no ws argument,
+    no allocation); calls on one GPU must not overlap in time."""
+    inp, out = _block_args(shape, inputs, outputs)
+    _check(_lib.verify_block_noalloc(C.byref(shape), C.byref(inp), C.byref(out),
+                                     _stream(stream)), "verify_block_noalloc")
 
 
 def acceptmoe_cache_plan(state: CacheState, active) -> list:

@@ -169,3 +169,13 @@ def check_selection(gpu: dict, ref: dict, stats: dict, cfg, ctx=""):
 def max_rel_err(y_gpu: torch.Tensor, y_ref: np.ndarray) -> float:
     y = y_gpu.float().cpu().numpy().astype(np.float64)
     return float(np.max(np.abs(y - y_ref)) / np.max(np.abs(y_ref)))
+
+
+def oracle_layer_args(cfg, b, w, logits, resident="block"):
+    """Keyword arguments of oracle.verify_block for a block run with the GPU's
+    fp32 logits (the selection is then bit-exact to compare)."""
+    return dict(k=cfg.k, x=W.to_exact_f64(b.x), expert_fn=expert_fn_from(cfg, w),
+                parent=b.parent, depth=b.depth, commit=b.commit, logits_in=logits,
+                resident=b.resident if isinstance(resident, str) else resident,
+                min_set=cfg.min_set, fixed_budget=cfg.fixed_budget,
+                reroute_budget=cfg.reroute, flags=cfg.flags, shared_fn=shared_fn_from(cfg, w))

@@ -172,3 +172,20 @@ def test_python_wrappers_reject_host_tensors(m):
     with pytest.raises(ValueError):
         m.acceptmoe_select(s, x, x, None, None, None, None, None, None, None, None, None,
                            None, None, None)
+
+
+def test_noalloc_rejects_a_block_beyond_its_workspace(m):
+    """verify_block_noalloc holds a fixed device workspace: a block that
+    needs more (256 nodes of hidden size 7168) is refused before any launch."""
+    lib = m.raw()
+    sh = _shape(m, N=256, H=7168, I=2048, E=256, k=8, n_depth=8, w_dtype=m.FP8_E4M3FN)
+    assert m.acceptmoe_workspace_size(sh) > m.NOALLOC_WORKSPACE_BYTES
+    inp = m.Inputs(*([FAKE.value] * 16))
+    out = m.Outputs(*([FAKE.value] * 8))
+    assert lib.verify_block_noalloc(C.byref(sh), C.byref(inp), C.byref(out), None) == m.EINVAL
+    assert b"NOALLOC_WORKSPACE_BYTES" in lib.acceptmoe_last_error()
+    # and argument errors come first, as for verify_block
+    assert lib.verify_block_noalloc(None, C.byref(inp), C.byref(out), None) == m.EINVAL
+    sh64 = _shape(m)
+    assert m.acceptmoe_workspace_size(sh64) <= m.NOALLOC_WORKSPACE_BYTES
+    assert lib.verify_block_noalloc(C.byref(sh64), None, C.byref(out), None) == m.EINVAL
