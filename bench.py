@@ -344,6 +344,13 @@ def main():
     achieved = sum(gate_bytes) / (sum(g_us) * 1e-6) / 1e9
     log("stages (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
 
+    # the same blocks through verify_block (no side stream), for comparison
+    serial = None
+    if layers[0].ovl is not None:
+        serial = time_variants(M, torch, layers, dblocks, slots, S, args.variant_steps,
+                               [("serial", dict(overlap=False))])["serial"]["us_per_block"]
+        log(f"verify_block without the side stream: {serial:.2f} us/block")
+
     # ------------------------------------------- selector variants (same kernels) --
     variants = None
     if not args.no_variants:
@@ -374,8 +381,10 @@ def main():
         "config": {"workload": f"{cfg.name}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} "
                                f"N={cfg.N}-node tree, {cfg.act} act / {cfg.w} experts",
                    "layers_rotated": args.layers, "blocks_rotated": args.blocks,
-                   "launch": "eager" if args.eager else
-                   f"hip-graph replay, {S} blocks per graph (a stack of MoE layers)",
+                   "launch": ("eager" if args.eager else
+                              f"hip-graph replay, {S} blocks per graph (a stack of MoE layers)")
+                   + ("; verify_block_overlap: the shared expert on a side stream"
+                      if layers[0].ovl is not None else ""),
                    "flags": cfg.flags, "fixed_budget": cfg.fixed_budget},
         "throughput": {"blocks_per_s": round(1e6 / us_block, 1),
                        "verify_nodes_per_s": round(cfg.N * 1e6 / us_block, 1),
@@ -385,6 +394,7 @@ def main():
                        "unique_expert_frac_of_copy": round(uniq_gbps / copy_gbps, 4)},
         "latency_us": latency,
         "us_per_block_one_graph_per_block": None if us_single is None else round(us_single, 3),
+        "us_per_block_without_side_stream": serial,
         "selection": {"U_mean": statistics.mean(U), "U_by_block": U,
                       "eligible_mean": statistics.mean(st["n_eligible"] for st in stats),
                       "natural_union_mean": statistics.mean(st["n_natural_union"] for st in stats),
@@ -621,7 +631,12 @@ def time_variants(M, torch, layers, dblocks, slots, S, steps, plan):
     selection statistics."""
     res = {}
     for name, fields in plan:
+        fields = dict(fields)
+        ov = fields.pop("overlap", None)
         vl = [layer.variant(**fields) for layer in layers]
+        if ov is not None:
+            for v in vl:
+                v.set_overlap(ov)
 
         def run_v(s, vl=vl):
             bi, li = slots[s]

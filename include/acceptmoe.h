@@ -289,6 +289,39 @@ int verify_block(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
                  const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * verify_block_overlap -- verify_block with the layer's shared expert on a
+ * second stream, so it runs while the selection and the routed experts do.
+ * Same outputs, bit for bit.
+ *
+ * [MoE-SD blog, MoE layer]: an always-on shared expert adds its output to
+ * every token, unweighted; it depends on x alone, not on the routing, so it
+ * need not wait for the selection.  [EcoSpec, Fig. 1]: verification time is
+ * the experts' weight traffic; streaming the shared expert's weights next to
+ * the selection (which moves little) takes them off the block's critical
+ * path.  The side stream forks from `stream` at the start of the call and is
+ * joined back into it before the combine.  Without a shared expert, or with
+ * F32 weights, the call is verify_block.
+ *
+ *   ov->side   a second stream of the caller, of the same (default) priority
+ *              as `stream`, not `stream` itself; the call is still ordered
+ *              as a whole on `stream`, and can be captured in a HIP graph (the
+ *              side stream joins the capture through the events)
+ *   ov->start, ov->done   two events of the caller, re-recorded by every call
+ *              (timing may be disabled)
+ *   ws         as verify_block
+ * Calls that share a workspace or a side stream must not overlap in time.
+ * ------------------------------------------------------------------------- */
+typedef struct acceptmoe_overlap {
+  hipStream_t side;
+  hipEvent_t start;
+  hipEvent_t done;
+} acceptmoe_overlap;
+
+int verify_block_overlap(const acceptmoe_shape* shape, const acceptmoe_inputs* in,
+                         const acceptmoe_outputs* out, const acceptmoe_overlap* ov, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * verify_block_noalloc -- verify_block for callers that cannot allocate
  * device memory (code under HIP graph capture, serving loops or harnesses
  * that never call hipMalloc): the workspace is the library's own device

@@ -55,6 +55,10 @@ class Outputs(C.Structure):
         "y", "logits_out", "eligible", "topk_idx", "topk_gate", "counts", "active", "stats")]
 
 
+class Overlap(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("side", "start", "done")]
+
+
 class CacheState(C.Structure):
     _fields_ = [("E", C.c_int32), ("n_slots", C.c_int32), ("n_spill", C.c_int32),
                 ("_pad", C.c_int32), ("slot_expert", C.c_void_p), ("expert_slot", C.c_void_p),
@@ -104,6 +108,7 @@ def _load():
         "acceptmoe_workspace_size": (sz, [vp]),
         "verify_block": (C.c_int, [vp, vp, vp, vp, sz, vp]),
         "verify_block_noalloc": (C.c_int, [vp, vp, vp, vp]),
+        "verify_block_overlap": (C.c_int, [vp, vp, vp, vp, vp, sz, vp]),
         "acceptmoe_cache_plan": (C.c_int, [vp, vp, i32, vp, vp, vp]),
         "verify_block_cached": (C.c_int, [vp, vp, vp, vp, vp, vp, sz, vp]),
         "acceptmoe_set_stage_timer": (C.c_int, [i32, vp, vp]),
@@ -122,7 +127,7 @@ _lib = _load()
 EXPORTED = ("acceptmoe_select_workspace_size", "acceptmoe_select", "moe_route_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "acceptmoe_packed_size", "acceptmoe_pack_experts",
-            "acceptmoe_workspace_size", "verify_block", "verify_block_noalloc",
+            "acceptmoe_workspace_size", "verify_block", "verify_block_noalloc", "verify_block_overlap",
             "acceptmoe_cache_plan",
             "verify_block_cached", "acceptmoe_set_stage_timer",
             "acceptmoe_strerror",
@@ -360,6 +365,17 @@ def verify_block(shape: Shape, inputs: dict, outputs: dict, ws, stream=None):
     _check(_lib.verify_block(C.byref(shape), C.byref(inp), C.byref(out),
                              _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0,
                              _stream(stream)), "verify_block")
+
+
+def verify_block_overlap(shape: Shape, inputs: dict, outputs: dict, overlap: "Overlap", ws,
+                         stream=None):
+    """verify_block with the shared expert on the side stream of `overlap`
+    while the selection and the routed experts run (same outputs)."""
+    inp, out = _block_args(shape, inputs, outputs)
+    _check(_lib.verify_block_overlap(C.byref(shape), C.byref(inp), C.byref(out),
+                                     C.byref(overlap), _ptr(ws, "ws", torch.uint8),
+                                     ws.numel() if ws is not None else 0, _stream(stream)),
+           "verify_block_overlap")
 
 
 NOALLOC_WORKSPACE_BYTES = 16 << 20  # the library's own workspace of verify_block_noalloc

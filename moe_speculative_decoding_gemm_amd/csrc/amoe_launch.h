@@ -116,6 +116,11 @@ struct GroupedArgs {
   // see permute_block): a grid of whole rounds of one work-group per CU
   // deals the items in a snake over the rounds
   int snake;
+  // bf16 / fp8, when > 0: dense mode -- dense_n experts (active[0..dense_n),
+  // or 0..dense_n-1 when active is null; offsets, sorted_assign and
+  // n_active unused) each over all N rows: row m of expert u is node m's x,
+  // written to row u*N + m of h_perm and y_perm
+  int dense_n;
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);
@@ -126,10 +131,15 @@ size_t packed_bytes(int which, int w_kind, int E, int H, int I);
 hipError_t launch_pack(int which, int w_kind, int E, int H, int I, const void* src, void* dst,
                        hipStream_t stream);
 
-// inv_pos == nullptr: y_perm rows are in token-major assignment order
-hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm,
-                          const int32_t* inv_pos, const float* topk_gate, const float* y_shared,
-                          void* y, hipStream_t stream);
+struct CombineArgs {
+  int N, k, H, act_bf16;
+  const float* y_perm;
+  const int32_t* inv_pos;  // nullptr: y_perm rows are in token-major order (i*k + j)
+  const float* gate;       // [N][k]
+  const float* y_shared;   // [N][H] or nullptr
+  void* y;                 // [N][H] act dtype
+};
+hipError_t launch_combine(const CombineArgs& c, hipStream_t stream);
 
 // identity grouping for the shared expert: offsets {0,N}, sorted_assign 0..N-1,
 // active {0}, n_active {1}

@@ -492,12 +492,56 @@ int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
 
 namespace {
 
+// The shared expert's two projections, in dense mode over all N rows (bf16 /
+// fp8; fp32 weights take the identity grouping), on `stream`.
+int launch_shared(const acceptmoe_shape* s, const acceptmoe_inputs* in, const VerifyWs& w,
+                  const amoe::GroupedArgs& g, hipStream_t stream) {
+  amoe::GroupedArgs gs = g;
+  gs.k = 1;
+  gs.E = 1;
+  gs.w13 = in->w13_shared;
+  gs.w2 = in->w2_shared;
+  gs.s13 = in->s13_shared;
+  gs.s2 = in->s2_shared;
+  gs.y_perm = w.sh_y;
+  gs.h_perm = w.sh_h;
+  gs.tok_rows = 0;
+  gs.w_slot = nullptr;
+  gs.n_wslots = 0;
+  gs.max_rows = nullptr;
+  gs.groups = nullptr;
+  gs.snake = 0;
+  gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
+  if (g.w_kind != 0) {
+    gs.dense_n = 1;
+    gs.active = nullptr;
+    gs.n_active = nullptr;
+    gs.offsets = nullptr;
+    gs.sorted_assign = nullptr;
+  } else {
+    int rc = hip_status(amoe::launch_shared_grouping(s->N, w.sh_offsets, w.sh_sorted,
+                                                     w.sh_active, w.sh_n_active, stream),
+                        "verify_block/shared grouping");
+    if (rc) return rc;
+    gs.dense_n = 0;
+    gs.offsets = w.sh_offsets;
+    gs.sorted_assign = w.sh_sorted;
+    gs.active = w.sh_active;
+    gs.n_active = w.sh_n_active;
+  }
+  return hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
+}
+
 // verify_block, and with `cache` set verify_block_cached: the expert weights
 // then come from the cache's device slots, after the missing ones are copied
-// in (one stream synchronization after the selection)
+// in (one stream synchronization after the selection).  With `ov` set
+// (verify_block_overlap), the shared expert, which depends on x alone, runs
+// on the caller's side stream while the selection and the routed experts
+// run, and is joined before the combine.
 int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
               const acceptmoe_expert_cache* cache, const acceptmoe_outputs* out,
-              acceptmoe_cache_report* report, void* ws, size_t ws_bytes, hipStream_t stream) {
+              acceptmoe_cache_report* report, const acceptmoe_overlap* ov, void* ws,
+              size_t ws_bytes, hipStream_t stream) {
   size_t need = 0;
   int rc = check_block_args(s, in, cache, out, &need);
   if (rc) return rc;
@@ -505,6 +549,9 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   if (ws_bytes < need)
     return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
   const bool shared = in->w13_shared != nullptr;
+  const int wk = w_kind(s->w_dtype);
+  // the shared expert (bf16 / fp8 weights) on the side stream
+  const bool sh_side = ov != nullptr && !cache && wk != 0 && shared;
 
   Carver c(ws);
   const VerifyWs w = carve_verify(c, s, shared);
@@ -539,22 +586,14 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   a.max_rows = w.n_active + 1;
   a.groups = w.groups;
   a.active_w = w.active_w;
-  timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
-  rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
-  if (rc) return rc;
-  timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
-  bool overlap = false;
-  if (cache) {
-    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
-    if (rc) return rc;
-  }
-  amoe::GroupedArgs g;
+
+  amoe::GroupedArgs g = {};
   g.N = s->N;
   g.k = s->k;
   g.E = s->E;
   g.H = s->H;
   g.I = s->I;
-  g.w_kind = w_kind(s->w_dtype);
+  g.w_kind = wk;
   g.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
   g.x = in->x;
   g.w13 = cache ? cache->dev_w13 : in->w13;
@@ -563,24 +602,47 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.s2 = in->s2;
   g.offsets = w.offsets;
   g.sorted_assign = w.sorted_assign;
-  // the expert kernels take the active experts most-routed first: the work
-  // items of the few experts with many rows (the longest ones) then start on
-  // separate CUs, and the lightest items are the ones that share a CU last
-  g.active = w.active_w;
-  g.snake = 1;
-  g.n_active = w.n_active;
   g.y_perm = w.y_perm;
   g.h_perm = w.h_perm;
   g.num_cu = num_cu();
   g.packed = s->w_layout == ACCEPTMOE_LAYOUT_PACKED;
   // bf16 / fp8 weights: the down projection writes token-major rows, so the
   // combine gathers without inv_pos (same values, same arithmetic)
-  g.tok_rows = g.w_kind != 0;
+  g.tok_rows = wk != 0;
   g.row_groups = 1;
-  g.max_rows = w.n_active + 1;
-  g.groups = w.groups;
   g.w_slot = cache ? cache->dev_expert_slot : nullptr;
   g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
+
+  if (sh_side) {
+    // the side stream starts after everything enqueued on `stream` before
+    // the call; the main chain is enqueued first, so a graph captured from
+    // the call keeps it on one queue
+    rc = hip_status(hipEventRecord(ov->start, stream), "verify_block_overlap/fork");
+    if (rc) return rc;
+  }
+  timer_mark(ACCEPTMOE_STAGE_SELECT, true, stream);
+  rc = hip_status(amoe::launch_select(a, stream), "verify_block/select");
+  if (rc) return rc;
+  timer_mark(ACCEPTMOE_STAGE_SELECT, false, stream);
+  if (sh_side) {
+    rc = hip_status(hipStreamWaitEvent(ov->side, ov->start, 0), "verify_block_overlap/fork");
+    if (!rc) rc = launch_shared(s, in, w, g, ov->side);
+    if (!rc) rc = hip_status(hipEventRecord(ov->done, ov->side), "verify_block_overlap/join");
+    if (rc) return rc;
+  }
+  bool overlap = false;
+  if (cache) {
+    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
+    if (rc) return rc;
+  }
+  // the expert kernels take the active experts most-routed first: the work
+  // items of the few experts with many rows (the longest ones) then start on
+  // separate CUs, and the lightest items are the ones that share a CU last
+  g.active = w.active_w;
+  g.n_active = w.n_active;
+  g.snake = 1;
+  g.max_rows = w.n_active + 1;
+  g.groups = w.groups;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   if (overlap) {
     // the hit experts while the missing ones are copied in, then those (the
@@ -610,38 +672,25 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   }
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, false, stream);
   timer_mark(ACCEPTMOE_STAGE_COMBINE, true, stream);
-  if (shared) {
-    rc = hip_status(amoe::launch_shared_grouping(s->N, w.sh_offsets, w.sh_sorted, w.sh_active,
-                                                 w.sh_n_active, stream),
-                    "verify_block/shared grouping");
-    if (rc) return rc;
-    amoe::GroupedArgs gs = g;
-    gs.k = 1;
-    gs.E = 1;
-    gs.w13 = in->w13_shared;
-    gs.w2 = in->w2_shared;
-    gs.s13 = in->s13_shared;
-    gs.s2 = in->s2_shared;
-    gs.offsets = w.sh_offsets;
-    gs.sorted_assign = w.sh_sorted;
-    gs.active = w.sh_active;
-    gs.n_active = w.sh_n_active;
-    gs.y_perm = w.sh_y;
-    gs.h_perm = w.sh_h;
-    gs.tok_rows = 0;
-    gs.w_slot = nullptr;
-    gs.max_rows = nullptr;
-    gs.groups = nullptr;
-    gs.snake = 0;
-    gs.n_wslots = 0;
-    gs.row_groups = (s->N + 63) / 64;  // the shared expert takes all N rows
-    rc = hip_status(amoe::launch_grouped(gs, stream), "verify_block/shared expert");
+  if (shared && !sh_side) {
+    rc = launch_shared(s, in, w, g, stream);
     if (rc) return rc;
   }
-  rc = hip_status(amoe::launch_combine(s->N, s->k, s->H, s->act_dtype == ACCEPTMOE_BF16,
-                                       w.y_perm, g.tok_rows ? nullptr : w.inv_pos, topk_gate,
-                                       shared ? w.sh_y : nullptr, out->y, stream),
-                  "verify_block/combine");
+  if (sh_side) {
+    rc = hip_status(hipStreamWaitEvent(stream, ov->done, 0), "verify_block_overlap/join");
+    if (rc) return rc;
+  }
+  amoe::CombineArgs cb = {};
+  cb.N = s->N;
+  cb.k = s->k;
+  cb.H = s->H;
+  cb.act_bf16 = s->act_dtype == ACCEPTMOE_BF16;
+  cb.y_perm = w.y_perm;
+  cb.inv_pos = g.tok_rows ? nullptr : w.inv_pos;
+  cb.gate = topk_gate;
+  cb.y_shared = shared ? w.sh_y : nullptr;
+  cb.y = out->y;
+  rc = hip_status(amoe::launch_combine(cb, stream), "verify_block/combine");
   timer_mark(ACCEPTMOE_STAGE_COMBINE, false, stream);
   return rc;
 }
@@ -762,7 +811,7 @@ int moe_grouped_swiglu(int32_t N, int32_t k, int32_t E, int32_t H, int32_t I,
   const size_t need = moe_grouped_swiglu_workspace_size(N, k, I, w_dtype);
   if (ws_bytes < need)
     return fail(ACCEPTMOE_EINVAL, "workspace %zu bytes < %zu required", ws_bytes, need);
-  amoe::GroupedArgs a;
+  amoe::GroupedArgs a = {};
   a.N = N;
   a.k = k;
   a.E = E;
@@ -803,9 +852,17 @@ int moe_combine(int32_t N, int32_t k, int32_t H, int32_t act_dtype, const float*
     return fail(ACCEPTMOE_EINVAL, "bad sizes N=%d k=%d H=%d", N, k, H);
   if (!y_perm || !inv_pos || !topk_gate || !y)
     return fail(ACCEPTMOE_EINVAL, "a required pointer is NULL");
-  return hip_status(amoe::launch_combine(N, k, H, act_dtype == ACCEPTMOE_BF16, y_perm, inv_pos,
-                                         topk_gate, y_shared, y, stream),
-                    "moe_combine");
+  amoe::CombineArgs cb = {};
+  cb.N = N;
+  cb.k = k;
+  cb.H = H;
+  cb.act_bf16 = act_dtype == ACCEPTMOE_BF16;
+  cb.y_perm = y_perm;
+  cb.inv_pos = inv_pos;
+  cb.gate = topk_gate;
+  cb.y_shared = y_shared;
+  cb.y = y;
+  return hip_status(amoe::launch_combine(cb, stream), "moe_combine");
 }
 
 size_t acceptmoe_packed_size(const acceptmoe_shape* s, int32_t which, int32_t n_experts) {
@@ -849,7 +906,18 @@ size_t acceptmoe_workspace_size(const acceptmoe_shape* s) {
 
 int verify_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
                  const acceptmoe_outputs* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return run_block(s, in, nullptr, out, nullptr, ws, ws_bytes, stream);
+  return run_block(s, in, nullptr, out, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int verify_block_overlap(const acceptmoe_shape* s, const acceptmoe_inputs* in,
+                         const acceptmoe_outputs* out, const acceptmoe_overlap* ov, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (!ov || !ov->side || !ov->start || !ov->done)
+    return fail(ACCEPTMOE_EINVAL, "verify_block_overlap: a side stream and two events are "
+                "required");
+  if (ov->side == stream)
+    return fail(ACCEPTMOE_EINVAL, "verify_block_overlap: the side stream is the call's stream");
+  return run_block(s, in, nullptr, out, nullptr, ov, ws, ws_bytes, stream);
 }
 
 int verify_block_cached(const acceptmoe_shape* s, const acceptmoe_inputs* in,
@@ -857,7 +925,7 @@ int verify_block_cached(const acceptmoe_shape* s, const acceptmoe_inputs* in,
                         acceptmoe_cache_report* report, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
   if (!cache) return fail(ACCEPTMOE_EINVAL, "cache is NULL");
-  return run_block(s, in, cache, out, report, ws, ws_bytes, stream);
+  return run_block(s, in, cache, out, report, nullptr, ws, ws_bytes, stream);
 }
 
 int acceptmoe_cache_plan(acceptmoe_cache_state* st, const int32_t* active, int32_t n_active,

@@ -434,7 +434,11 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
   const int H = a.H, I = a.I, k = a.k;
   const int K = GATEUP ? H : I;
   const int tiles = (GATEUP ? 2 * I : H) / (64 * NT);
-  const int n_items = *a.n_active * tiles;
+  // dense mode: a.dense_n experts (a.active[0..dense_n), or expert u when
+  // a.active is null) over every one of the N rows: expert u's rows are
+  // u*N .. u*N+N-1 of h_perm / y_perm, row m being node m's x
+  const bool dense = a.dense_n > 0;
+  const int n_items = (dense ? a.dense_n : *a.n_active) * tiles;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 15, g = lane >> 4;
   const int nchunks = (K + KC - 1) / KC;
   // packed weights are zero-padded to whole chunks: every step is computed
@@ -449,7 +453,8 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
   // than 64 routed rows, (64-row group, tile) pairs from the groups table
   // (group-major, so the groups of one tile are `tiles` units apart and read
   // its weights at about the same time).
-  const bool by_group = a.groups != nullptr && a.max_rows != nullptr && *a.max_rows > ROWS;
+  const bool by_group =
+      !dense && a.groups != nullptr && a.max_rows != nullptr && *a.max_rows > ROWS;
   const int n_units = by_group ? a.groups[0] * tiles : n_items * R;
   // snake: the active list comes heaviest first and the grid is whole rounds
   // of one work-group per CU (work-group b, b + C, b + 2C, .. share CU b % C
@@ -480,9 +485,9 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
       tile = item - u * tiles;
       rstep = R;
     }
-    const int e = a.active[u];
-    const int off = a.offsets[e];
-    const int te = a.offsets[e + 1] - off;
+    const int e = dense ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
+    const int off = dense ? u * a.N : a.offsets[e];
+    const int te = dense ? a.N : a.offsets[e + 1] - off;
     // where expert e's weights sit
     const int ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
 
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         for (int p = 0; p < PV; ++p) {
           const int rr = p * RPP + t / TPR;
           const int m = mg + rr < te ? mg + rr : mg;
-          const int srcrow = GATEUP ? a.sorted_assign[off + m] / k : off + m;
+          const int srcrow = GATEUP ? (dense ? m : a.sorted_assign[off + m] / k) : off + m;
           src[p] = src_base + static_cast<size_t>(srcrow) * src_ld;
         }
         f32x4_t acc[NT][MTV];
@@ -640,7 +645,7 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         for (int d = 1; d < DW; ++d) load_b(bq[d], bsc[d], min(d, nchunks - 1));
         // down, token-major output: each routed row's assignment index, loaded
         // behind the pipeline's loads and used only by the epilogue
-        const bool tok = !GATEUP && a.tok_rows;
+        const bool tok = !GATEUP && a.tok_rows && !dense;
         int my_row = 0;
         if (tok) my_row = a.sorted_assign[off + min(mg + lane, te - 1)];
         stage_store(sv[0], 0);
@@ -792,7 +797,7 @@ template <int WK, int NT, int KC, bool PACKED>
 void launch_lds(const GroupedArgs& a, hipStream_t stream, int which) {
   static const int occ_g = resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED>, 2);
   static const int occ_d = resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED>, 2);
-  const int max_active = a.E < a.N * a.k ? a.E : a.N * a.k;
+  const int max_active = a.dense_n > 0 ? a.dense_n : (a.E < a.N * a.k ? a.E : a.N * a.k);
   const int R = a.row_groups > 1 ? a.row_groups : 1;
   if (which != 2) {
     const int items = max_active * (2 * a.I / (64 * NT)) * R;

@@ -42,30 +42,27 @@ __global__ void shared_grouping_kernel(int N, int32_t* offsets, int32_t* sorted_
 // kTok: the rows are already in token-major order (row i*k + j), so the
 // loads need no inv_pos round trip first; the arithmetic is the same.
 template <bool kBf16, bool kTok>
-__global__ __launch_bounds__(256) void combine_kernel(int N, int k, int H,
-                                                      const float* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ inv_pos,
-                                                      const float* __restrict__ gate,
-                                                      const float* __restrict__ y_shared,
-                                                      void* __restrict__ y) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
+  const int N = c.N, k = c.k, H = c.H;
   const int h4 = H >> 2;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<size_t>(N) * h4) return;
   const int i = static_cast<int>(idx / h4);
   const int h = static_cast<int>(idx - static_cast<size_t>(i) * h4) * 4;
-  int row[kMaxK];
+  const float* src[kMaxK];
   float g[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
-      row[j] = kTok ? i * k + j : inv_pos[static_cast<size_t>(i) * k + j];
-      g[j] = gate[static_cast<size_t>(i) * k + j];
+      const int row = kTok ? i * k + j : c.inv_pos[static_cast<size_t>(i) * k + j];
+      src[j] = c.y_perm + static_cast<size_t>(row) * H;
+      g[j] = c.gate[static_cast<size_t>(i) * k + j];
     }
   }
   f32x4_t v[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (j < k) v[j] = *reinterpret_cast<const f32x4_t*>(y_perm + static_cast<size_t>(row[j]) * H + h);
+    if (j < k) v[j] = *reinterpret_cast<const f32x4_t*>(src[j] + h);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
@@ -73,15 +70,24 @@ __global__ __launch_bounds__(256) void combine_kernel(int N, int k, int H,
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(g[j], v[j][q], acc[q]);
     }
-  if (y_shared) acc += *reinterpret_cast<const f32x4_t*>(y_shared + static_cast<size_t>(i) * H + h);
+  if (c.y_shared)
+    acc += *reinterpret_cast<const f32x4_t*>(c.y_shared + static_cast<size_t>(i) * H + h);
   if (kBf16) {
     u32x2_t o;
     o[0] = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
     o[1] = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(y) + static_cast<size_t>(i) * H + h) = o;
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(c.y) + static_cast<size_t>(i) * H + h) = o;
   } else {
-    *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + static_cast<size_t>(i) * H + h) = acc;
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(c.y) + static_cast<size_t>(i) * H + h) = acc;
   }
+}
+
+template <bool kBf16>
+void launch_combine_t(const CombineArgs& c, unsigned blocks, hipStream_t stream) {
+  if (c.inv_pos)
+    combine_kernel<kBf16, false><<<blocks, 256, 0, stream>>>(c);
+  else
+    combine_kernel<kBf16, true><<<blocks, 256, 0, stream>>>(c);
 }
 
 }  // namespace
@@ -103,26 +109,13 @@ hipError_t launch_shared_grouping(int N, int32_t* offsets, int32_t* sorted_assig
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int N, int k, int H, int act_bf16, const float* y_perm,
-                          const int32_t* inv_pos, const float* topk_gate, const float* y_shared,
-                          void* y, hipStream_t stream) {
-  const size_t n = static_cast<size_t>(N) * (H / 4);
+hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
+  const size_t n = static_cast<size_t>(c.N) * (c.H / 4);
   const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
-  if (act_bf16) {
-    if (inv_pos)
-      combine_kernel<true, false><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
-                                                              y_shared, y);
-    else
-      combine_kernel<true, true><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos, topk_gate,
-                                                             y_shared, y);
-  } else {
-    if (inv_pos)
-      combine_kernel<false, false><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos,
-                                                               topk_gate, y_shared, y);
-    else
-      combine_kernel<false, true><<<blocks, 256, 0, stream>>>(N, k, H, y_perm, inv_pos,
-                                                              topk_gate, y_shared, y);
-  }
+  if (c.act_bf16)
+    launch_combine_t<true>(c, blocks, stream);
+  else
+    launch_combine_t<false>(c, blocks, stream);
   return hipGetLastError();
 }
 

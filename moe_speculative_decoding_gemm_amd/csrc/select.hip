@@ -294,6 +294,35 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
 }
 
 // ------------------------------------------------------- set selection ----
+// Every arrival counter of the workspace must be zero between kernels of a
+// call: the front kernel's elections leave its group counters at zero and
+// note any count outside its range in counters[0].  A nonzero counter here
+// means the workspace was not zero-filled before its first use, or was
+// shared by calls that overlap: the call's outputs are then flagged
+// (kErrWorkspace), and the counters are set back to zero so that the
+// restricted kernel of this call and later calls elect correctly.  The tail
+// kernel's threads load the nwg + 2 counters (counters[0..1], then the node
+// groups' gcount) with the kernel's other first loads; select_set checks and
+// repairs them.
+struct CounterCheck {
+  int* ptr[2];  // this thread's counters (at most two), or null
+  int val[2];
+};
+__device__ __forceinline__ CounterCheck load_counters(const SelectArgs& a, int nwg) {
+  CounterCheck c;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int g = static_cast<int>(threadIdx.x) + r * kTail;
+    c.ptr[r] = nullptr;
+    c.val[r] = 0;
+    if (g < nwg + 2) {
+      c.ptr[r] = g < 2 ? &a.counters[g] : &a.gcount[g - 2];
+      c.val[r] = __hip_atomic_load(c.ptr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return c;
+}
+
 // Rank of expert t among the experts by counting over key[0..EP), where key
 // holds the demand of the experts that take part and a sentinel for the rest
 // (below or above every demand, so it never counts).  desc: order (key desc,
@@ -337,11 +366,11 @@ __device__ __forceinline__ int split_rank(const double* key, int* scratch, int E
 }
 
 // One kTail-thread work-group.  nwg partial rows (per expert, expert-major)
-// of demand / flags, nwg error words; ws_err: error bits found by the
-// workspace check (OR-ed in by any thread).  Leaves the eligible flags in
+// of demand / flags, nwg error words; cc: this thread's arrival counter as
+// loaded at the start of the kernel (checked and set back to zero here).  Leaves the eligible flags in
 // sm.elig (and in a.eligible), statistics in a.stats (n_active and
 // n_active_nonresident follow once the restricted top-k is known).
-__device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm, int ws_err) {
+__device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm, CounterCheck cc) {
   static_assert(kMaxE == 256 && kTail >= kMaxE, "select_set keeps one thread per expert slot");
   const int t = threadIdx.x;
   const int E = a.E, k = a.k;
@@ -397,7 +426,14 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm, int ws_err
     sm.key[t] = in_fill ? dsum : -1.0;
     sm.elig[t] = in_fill;
   }
-  if (err0 | ws_err) atomicOr(&sm.err, err0 | ws_err);
+  if (err0) atomicOr(&sm.err, err0);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (cc.val[r] != 0) {
+      atomicOr(&sm.err, kErrWorkspace);
+      __hip_atomic_store(cc.ptr[r], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   for (int w = t + kTail; w < nwg; w += kTail) {
     const int e = a.e_part[w];
     if (e) atomicOr(&sm.err, e);
@@ -831,35 +867,15 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
 // The set selection and, for N <= kFusedMaxN, every node's restricted top-k,
 // the gates and the grouping: one work-group of kTail threads, after the
 // front kernel.  The node phase's outputs are loaded first, all together.
-// Every arrival counter of the workspace must be zero between kernels of a
-// call: the front kernel's elections leave its group counters at zero and
-// note any count outside its range in counters[0].  A nonzero counter here
-// means the workspace was not zero-filled before its first use, or was
-// shared by calls that overlap: the call's outputs are then flagged
-// (kErrWorkspace), and the counters are set back to zero so that the
-// restricted kernel of this call and later calls elect correctly.  Runs
-// before the tail kernel's first barrier; returns the error bits.
-__device__ __forceinline__ int check_counters(const SelectArgs& a, int nwg) {
-  int bad = 0;
-  for (int g = static_cast<int>(threadIdx.x); g < nwg + 2; g += kTail) {
-    int* c = g < nwg ? &a.gcount[g] : &a.counters[g - nwg];
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-      bad = kErrWorkspace;
-      __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  return bad;
-}
-
 __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) TailSmem sm;
   const int t = threadIdx.x;
   const int N = a.N, E = a.E;
   const int nwg = node_groups(N);
   const bool fused = N <= kFusedMaxN;
-  const int ws_err = check_counters(a, nwg);
+  const CounterCheck cc = load_counters(a, nwg);
   if (!fused) {
-    select_set(a, nwg, sm.set, ws_err);
+    select_set(a, nwg, sm.set, cc);
     return;
   }
   // natural top-k, its logits, max / sum of exp per node, and (when they
@@ -888,7 +904,7 @@ __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
     pm = a.node_m[t];
     pz = a.node_z[t];
   }
-  select_set(a, nwg, sm.set, ws_err);
+  select_set(a, nwg, sm.set, cc);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (x4 + j < NK) {

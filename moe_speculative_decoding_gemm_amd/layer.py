@@ -18,11 +18,15 @@ class VerifyLayer:
     (+ s13_shared/s2_shared).  All device tensors, row-major.  With pack=True
     (the default for BF16 / FP8 weights) the expert weights are reordered
     once into the packed layout the kernels stream fastest; the row-major
-    tensors are then not referenced.
+    tensors are then not referenced.  With overlap=True (the default for a
+    layer with a shared expert and BF16 / FP8 weights) run() calls
+    verify_block_overlap on a side stream of the layer's own (default
+    priority) and two events; overlap=False calls verify_block.  Both give the
+    same bits.
     """
 
     def __init__(self, shape: L.Shape, weights: dict, device=None, debug_outputs: bool = True,
-                 pack: Optional[bool] = None):
+                 pack: Optional[bool] = None, overlap: Optional[bool] = None):
         if pack is None:
             pack = shape.w_dtype != L.F32
         self.shape = L.Shape.from_buffer_copy(shape)
@@ -38,6 +42,9 @@ class VerifyLayer:
                                          weights["w2_shared"][None], 1)
                 self.w["w13_shared"], self.w["w2_shared"] = p13, p2
         self.device = dev
+        if overlap is None:
+            overlap = shape.w_dtype != L.F32 and weights.get("w13_shared") is not None
+        self.set_overlap(overlap)
         N, H, E, k = shape.N, shape.H, shape.E, shape.k
         adt = torch.float32 if shape.act_dtype == L.F32 else torch.bfloat16
         nbytes = L.acceptmoe_workspace_size(shape)
@@ -56,6 +63,19 @@ class VerifyLayer:
                 active=torch.empty(E, dtype=torch.int32, device=dev),
                 stats=torch.zeros(L.STATS_BYTES, dtype=torch.uint8, device=dev))
 
+    def set_overlap(self, on: bool):
+        """Use verify_block_overlap (on) or verify_block (off) in run()."""
+        self.ovl = None
+        if on:
+            if getattr(self, "_side", None) is None:
+                self._side = torch.cuda.Stream(device=self.device)
+                self._events = [torch.cuda.Event() for _ in range(2)]
+                for ev in self._events:  # creates the event handles
+                    ev.record(self._side)
+                torch.cuda.synchronize(self.device)
+            self.ovl = L.Overlap(self._side.cuda_stream,
+                                 *[ev.cuda_event for ev in self._events])
+
     def variant(self, **fields) -> "VerifyLayer":
         """A layer on the same (already packed) weights whose shape differs in
         the fields given (N, n_depth, flags, fixed_budget, min_set,
@@ -70,6 +90,9 @@ class VerifyLayer:
             setattr(v.shape, key, val)
         v.w = self.w
         v.device = self.device
+        v._side = getattr(self, "_side", None)
+        v._events = getattr(self, "_events", None)
+        v.ovl = self.ovl
         nbytes = L.acceptmoe_workspace_size(v.shape)
         if nbytes == 0:
             raise L.AcceptMoEError(L.EINVAL, "acceptmoe_workspace_size",
@@ -91,7 +114,10 @@ class VerifyLayer:
         inputs = dict(self.w)
         inputs.update(x=x, parent=parent, depth=depth, commit=commit, resident=resident,
                       logits_in=logits_in)
-        L.verify_block(self.shape, inputs, self.out, self.ws, stream=stream)
+        if self.ovl is not None:
+            L.verify_block_overlap(self.shape, inputs, self.out, self.ovl, self.ws, stream=stream)
+        else:
+            L.verify_block(self.shape, inputs, self.out, self.ws, stream=stream)
         return self.out
 
     def run_cached(self, cache, x, parent, depth, commit,
