@@ -414,12 +414,15 @@ int acceptmoe_set_stage_timer(int32_t stage, hipEvent_t start, hipEvent_t stop);
  * may be NULL) receives this call's counts.
  *
  * Overlap: with copy_stream, copy_done and dev_lists set (a stream of the
- * default priority, an event, 2E+2 device ints, all the caller's), the
- * missing experts are copied on copy_stream while the experts that hit run on
- * `stream`; `stream` then waits for copy_done and runs the fetched experts
- * ([MoE-SD blog, CPU offload section] counts the overlap of transfers
- * with compute among the measures of an offload system).  Results are identical: every
- * expert's rows are computed by the same kernels, only in two launches.
+ * default priority, an event, 2E+3 device ints, all the caller's), the
+ * missing experts are copied on copy_stream, one after another, while the
+ * experts that hit run on `stream`; each missing expert's kernels then run
+ * on `stream` as soon as its own copy has landed (copy_done is re-recorded
+ * after every copy), so the computation of one fetched expert overlaps the
+ * copy of the next ([MoE-SD blog, CPU offload section] counts the overlap
+ * of transfers with compute among the measures of an offload system).
+ * Results are identical: every expert's rows are computed by the same
+ * kernels, only in more launches.
  * ------------------------------------------------------------------------- */
 typedef struct acceptmoe_cache_state {
   int32_t E;              /* routed experts                                      */
@@ -444,7 +447,7 @@ typedef struct acceptmoe_expert_cache {
   uint8_t* dev_resident;          /* device [E]                                    */
   hipStream_t copy_stream;        /* or NULL: the copies run on the call's stream  */
   hipEvent_t copy_done;           /* with copy_stream                              */
-  int32_t* dev_lists;             /* device [2E+2], with copy_stream               */
+  int32_t* dev_lists;             /* device [2E+3], with copy_stream               */
 } acceptmoe_expert_cache;
 
 typedef struct acceptmoe_cache_report {  /* one verify_block_cached call      */

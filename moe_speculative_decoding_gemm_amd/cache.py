@@ -69,12 +69,13 @@ class ExpertCache:
 
     def set_overlap(self, on: bool):
         """Copy the missing experts on a stream of their own (default
-        priority) while the hit experts run, or on the call's stream."""
+        priority) while the hit experts run, each missing expert computed as
+        soon as its copy has landed; or copy them on the call's stream."""
         if on and getattr(self, "copy_stream", None) is None:
             self.copy_stream = torch.cuda.Stream(device=self.device)
             self.copy_done = torch.cuda.Event()
             self.copy_done.record(self.copy_stream)  # creates the event handle
-            self.dev_lists = torch.zeros(2 * self.E + 2, dtype=torch.int32, device=self.device)
+            self.dev_lists = torch.zeros(2 * self.E + 3, dtype=torch.int32, device=self.device)
             torch.cuda.synchronize(self.device)
         if on:
             self.desc.copy_stream = self.copy_stream.cuda_stream

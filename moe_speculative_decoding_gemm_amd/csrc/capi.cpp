@@ -367,16 +367,39 @@ int check_cache(const acceptmoe_shape* s, const acceptmoe_expert_cache* c) {
   return ACCEPTMOE_OK;
 }
 
+// The missing experts of one block: (expert, slot) in plan order, and the
+// bytes of one expert's packed weights.
+struct FetchPlan {
+  int nf = 0;
+  int32_t fe[256], fs[256];
+  size_t b13 = 0, b2 = 0;
+};
+
+// Host-to-device copy of fetched expert f's packed weights into its slot.
+hipError_t copy_expert(const acceptmoe_expert_cache* c, const FetchPlan& p, int f,
+                       hipStream_t cs) {
+  const char* h13 = static_cast<const char*>(c->host_w13);
+  const char* h2 = static_cast<const char*>(c->host_w2);
+  char* d13 = static_cast<char*>(c->dev_w13);
+  char* d2 = static_cast<char*>(c->dev_w2);
+  hipError_t e = hipMemcpyAsync(d13 + p.b13 * p.fs[f], h13 + p.b13 * p.fe[f], p.b13,
+                                hipMemcpyHostToDevice, cs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(d2 + p.b2 * p.fs[f], h2 + p.b2 * p.fe[f], p.b2, hipMemcpyHostToDevice, cs);
+  return e;
+}
+
 // After the selection: read the active experts back (one stream
-// synchronization), plan, copy the missing experts' packed weights from
-// host memory into their slots, then the slot table and resident mask.
+// synchronization), plan, upload the slot table and resident mask, and copy
+// the missing experts' packed weights from host memory into their slots --
+// unless the cache has a copy stream (*overlap): then the copies are left to
+// the caller, which interleaves them with the fetched experts' kernels.
 int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const int32_t* active,
                 const int32_t* n_active, acceptmoe_cache_report* report, hipStream_t stream,
-                bool* overlap) {
+                bool* overlap, FetchPlan* plan) {
   acceptmoe_cache_state* st = c->state;
   int32_t host_n = 0;
   int32_t host_active[256];
-  int32_t fe[256], fs[256];
   hipError_t e = hipMemcpyAsync(&host_n, n_active, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(host_active, active, sizeof(int32_t) * s->E, hipMemcpyDeviceToHost, stream);
@@ -386,30 +409,30 @@ int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const
   if (host_n < 0 || host_n > s->E)
     return fail(ACCEPTMOE_EINVAL, "verify_block_cached: device reported %d active experts", host_n);
   acceptmoe_cache_report rep;
+  int32_t* fe = plan->fe;
+  int32_t* fs = plan->fs;
   int nf = 0;
   rc = plan_fetches(st, host_active, host_n, fe, fs, &nf, &rep);
   if (rc) return rc;
   const int wk = w_kind(s->w_dtype);
-  const size_t b13 = amoe::packed_bytes(0, wk, 1, s->H, s->I);
-  const size_t b2 = amoe::packed_bytes(1, wk, 1, s->H, s->I);
-  const char* h13 = static_cast<const char*>(c->host_w13);
-  const char* h2 = static_cast<const char*>(c->host_w2);
-  char* d13 = static_cast<char*>(c->dev_w13);
-  char* d2 = static_cast<char*>(c->dev_w2);
+  plan->nf = nf;
+  plan->b13 = amoe::packed_bytes(0, wk, 1, s->H, s->I);
+  plan->b2 = amoe::packed_bytes(1, wk, 1, s->H, s->I);
+  const size_t b13 = plan->b13, b2 = plan->b2;
   // the slot table and resident mask first, on the launch stream: every
   // expert kernel of this block reads the table
   e = hipMemcpyAsync(c->dev_expert_slot, st->expert_slot, sizeof(int32_t) * s->E,
                      hipMemcpyHostToDevice, stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(c->dev_resident, st->resident, s->E, hipMemcpyHostToDevice, stream);
-  // with a copy stream, the hit and the missing experts run as two passes:
-  // lists [hits (E)] [n_hits] [misses (E)] [n_misses]
+  // with a copy stream, the hit experts run while the missing ones are
+  // copied in, then each missing expert as its copy lands:
+  // lists [hits (E)] [n_hits] [misses (E)] [n_misses] [1]
   *overlap = c->copy_stream != nullptr && c->copy_done != nullptr && c->dev_lists != nullptr &&
              nf > 0;
-  hipStream_t cs = *overlap ? c->copy_stream : stream;
   if (*overlap && e == hipSuccess) {
     const int E = s->E;
-    int32_t lists[2 * 256 + 2];
+    int32_t lists[2 * 256 + 3];
     uint8_t miss[256];
     std::memset(miss, 0, sizeof(miss));
     for (int f = 0; f < nf; ++f) miss[fe[f]] = 1;
@@ -421,17 +444,15 @@ int cache_fetch(const acceptmoe_shape* s, const acceptmoe_expert_cache* c, const
     for (int f = 0; f < nf; ++f) lists[E + 1 + f] = fe[f];
     for (int f = nf; f < E; ++f) lists[E + 1 + f] = 0;
     lists[2 * E + 1] = nf;
-    e = hipMemcpyAsync(c->dev_lists, lists, sizeof(int32_t) * (2 * E + 2), hipMemcpyHostToDevice,
+    lists[2 * E + 2] = 1;
+    e = hipMemcpyAsync(c->dev_lists, lists, sizeof(int32_t) * (2 * E + 3), hipMemcpyHostToDevice,
                        stream);
   }
-  timer_mark(ACCEPTMOE_STAGE_FETCH, true, cs);
-  for (int f = 0; f < nf && e == hipSuccess; ++f) {
-    e = hipMemcpyAsync(d13 + b13 * fs[f], h13 + b13 * fe[f], b13, hipMemcpyHostToDevice, cs);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(d2 + b2 * fs[f], h2 + b2 * fe[f], b2, hipMemcpyHostToDevice, cs);
+  if (!*overlap) {
+    timer_mark(ACCEPTMOE_STAGE_FETCH, true, stream);
+    for (int f = 0; f < nf && e == hipSuccess; ++f) e = copy_expert(c, *plan, f, stream);
+    timer_mark(ACCEPTMOE_STAGE_FETCH, false, stream);
   }
-  timer_mark(ACCEPTMOE_STAGE_FETCH, false, cs);
-  if (*overlap && e == hipSuccess) e = hipEventRecord(c->copy_done, cs);
   rc = hip_status(e, "verify_block_cached/fetch");
   if (rc) return rc;
   rep.h2d_bytes = static_cast<int64_t>(nf) * static_cast<int64_t>(b13 + b2);
@@ -631,8 +652,9 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
     if (rc) return rc;
   }
   bool overlap = false;
+  FetchPlan plan;
   if (cache) {
-    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap);
+    rc = cache_fetch(s, cache, active, w.n_active, report, stream, &overlap, &plan);
     if (rc) return rc;
   }
   // the expert kernels take the active experts most-routed first: the work
@@ -645,21 +667,34 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.groups = w.groups;
   timer_mark(ACCEPTMOE_STAGE_EXPERTS, true, stream);
   if (overlap) {
-    // the hit experts while the missing ones are copied in, then those (the
-    // row-group table indexes the full active list: not used for the two lists)
+    // the hit experts while the missing ones are copied in on the copy
+    // stream, then each missing expert once its own copy has landed (the
+    // event is re-recorded after every copy; each wait binds to the record
+    // enqueued just before it).  The row-group table indexes the full active
+    // list: not used for these lists.
     const int32_t* lists = cache->dev_lists;
+    hipStream_t cs = cache->copy_stream;
     g.groups = nullptr;
     g.snake = 0;
     g.active = lists;
     g.n_active = lists + s->E;
     rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/hit experts");
     if (rc) return rc;
-    rc = hip_status(hipStreamWaitEvent(stream, cache->copy_done, 0), "verify_block_cached/wait");
-    if (rc) return rc;
-    g.active = lists + s->E + 1;
-    g.n_active = lists + 2 * s->E + 1;
-    rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched experts");
-    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_FETCH, true, cs);
+    for (int f = 0; f < plan.nf; ++f) {
+      rc = hip_status(copy_expert(cache, plan, f, cs), "verify_block_cached/fetch");
+      if (!rc) {
+        if (f == plan.nf - 1) timer_mark(ACCEPTMOE_STAGE_FETCH, false, cs);
+        rc = hip_status(hipEventRecord(cache->copy_done, cs), "verify_block_cached/fetch");
+      }
+      if (!rc) rc = hip_status(hipStreamWaitEvent(stream, cache->copy_done, 0),
+                               "verify_block_cached/wait");
+      if (rc) return rc;
+      g.active = lists + s->E + 1 + f;
+      g.n_active = lists + 2 * s->E + 2;  // 1
+      rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched expert");
+      if (rc) return rc;
+    }
   } else {
     timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
     rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");
