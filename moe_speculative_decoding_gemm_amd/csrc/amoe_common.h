@@ -232,36 +232,4 @@ __device__ __forceinline__ bool last_arrival_dev(int* counter, int nblocks, int*
   return s_last_dev != 0;
 }
 
-// Last-arriver election: every thread of the work-group calls this after its
-// global writes.  Returns true in exactly one work-group of the nblocks that
-// count on the same counter -- the last to arrive -- after which that
-// work-group sees the other work-groups' writes.  Each wave first waits for
-// its own stores to reach the L2 of its XCD; after the barrier one thread
-// writes that L2 back (device-scope release) before it counts the arrival,
-// and the last arriver's thread acquires (invalidates its caches) before the
-// second barrier.  One device-scope fence per work-group, not one per wave:
-// each such fence writes back the L2 of its XCD, and many of them in flight
-// serialise.  The counter must be zero before the first arrival; the last
-// work-group resets it, so it stays zero between launches.  A count outside
-// [0, nblocks) is OR-ed into *misuse as kErrWorkspace (see last_arrival_dev).
-__device__ __forceinline__ bool last_block_done(int* counter, int nblocks, int* misuse) {
-  __shared__ int s_last;
-  wait_global_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    wait_global_stores();  // the write-back has completed
-    const int prev = atomicAdd(counter, 1);
-    const bool last = prev == nblocks - 1;
-    if (last) {
-      __threadfence();
-      *counter = 0;  // ready for the next use
-    }
-    if (prev < 0 || prev >= nblocks) atomicOr(misuse, kErrWorkspace);
-    s_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  return s_last != 0;
-}
-
 }  // namespace amoe

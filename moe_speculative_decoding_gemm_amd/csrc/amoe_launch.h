@@ -43,7 +43,7 @@ struct SelectArgs {
   double* d_part;      // [E][groups, padded] demand summed over each 4-node group
   uint8_t* f_part;     // [E][groups, padded] bit 0: a root routes to the expert, bit 1: some node does
   int32_t* e_part;     // [groups] error bits of each node group
-  int32_t* counters;   // [2]: [0] arrivals seen outside their range, [1] restricted-kernel arrivals
+  int32_t* counters;   // [2]: [0] arrivals seen outside their range, [1] reserved (zero)
   int32_t* gcount;     // [N/4]: K-slice arrivals per node group (zero between calls)
   // when non-null, the restricted top-k is followed by the grouping of the
   // assignments by expert (moe_route_permute's outputs)

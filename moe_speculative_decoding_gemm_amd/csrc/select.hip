@@ -31,7 +31,8 @@
 // largest of any superset of them); the others rank their set members' keys
 // by counting.
 // For N > kFusedMaxN a third kernel (restricted_kernel, one wave per node)
-// takes the restricted top-k and gates, and its last work-group groups.
+// takes the restricted top-k and gates, and a fourth (group_kernel, one
+// work-group of 1024 threads) groups the assignments.
 // Every reduction has a fixed order: two runs give identical bits.  Arrival
 // counters are left at zero by the last arriver, so a zero-filled workspace
 // stays valid across calls.
@@ -45,7 +46,8 @@ namespace amoe {
 namespace {
 
 constexpr int kMaxKSplit = 16;   // router K slices (partial sums per logit)
-constexpr int kNodesPerWG = 4;   // nodes per group (one wave each in the node phase)
+constexpr int kNodesPerWG = 4;   // nodes per group up to kFusedMaxN nodes (one wave each)
+constexpr int kNodesPerWGBig = 16;  // nodes per group above (all 16 MFMA rows, 4 per wave)
 constexpr int kMaxSlice = 2048;  // K elements per router slice
 constexpr int kFusedMaxN = 256;  // largest N whose restricted top-k runs in the tail
 constexpr int kKeyCap = 4096;    // (node, member) keys per rank-counting pass
@@ -53,9 +55,17 @@ constexpr int kLgCap = 8192;     // logits the tail holds in LDS (N * E up to th
 constexpr int kTail = 1024;      // threads of the tail kernel (one work-group)
 constexpr int kRankCountMax = 64;  // largest (padded) set whose restricted top-k counts ranks
 
+// nodes per group of the front kernel: 4 for blocks that the tail kernel
+// finishes (short latency chains), 16 above (a quarter of the router weight
+// re-reads and of the demand rows the tail sums)
+__host__ __device__ __forceinline__ int nodes_per_group(int N) {
+  return N > kFusedMaxN ? kNodesPerWGBig : kNodesPerWG;
+}
 // demand / flag partial rows are stored expert-major, one row of group
 // partials per expert, padded so that a row starts 16-byte aligned
-__host__ __device__ __forceinline__ int node_groups(int N) { return (N + kNodesPerWG - 1) / kNodesPerWG; }
+__host__ __device__ __forceinline__ int node_groups(int N) {
+  return (N + nodes_per_group(N) - 1) / nodes_per_group(N);
+}
 __host__ __device__ __forceinline__ int dpart_stride(int N) { return (node_groups(N) + 1) & ~1; }
 __host__ __device__ __forceinline__ int fpart_stride(int N) { return (node_groups(N) + 15) & ~15; }
 
@@ -102,9 +112,11 @@ struct RouterSteps {
 };
 
 // ------------------------------------------------------------------ LDS ----
+template <int NPW>
 struct NodeSmem {
-  double c[kNodesPerWG][kMaxE];  // demand terms per node
-  int flags[kMaxE];              // bit 0: a root routes here, bit 1: some node does
+  double c[NPW][kMaxE];  // demand terms per node
+  float lg[NPW > kNodesPerWG ? NPW : 1][kMaxE];  // logits, when one work-group takes all of K
+  int flags[kMaxE];      // bit 0: a root routes here, bit 1: some node does
   int err;
 };
 struct SetSmem {
@@ -153,13 +165,16 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 }
 
 // ---------------------------------------------------------- node phase ----
-// Node i on one wave: logits from the K-slice partials (+ bias) or from
-// logits_in, fp64 softmax statistics, natural top-k (written in slot order),
-// demand terms into sm.c[slot], anchor / natural-use flags, error bits.
-// d, p, dp, cf: depth, parent, parent's depth and commit[depth] of node i.
-template <int Q>
-__device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot, NodeSmem& sm,
-                                           int d, int p, int dp, float cf, const float* bias) {
+// Node i on one wave: logits from the K-slice partials (+ bias), from the
+// work-group's own product in LDS (lrow, when one work-group took all of K)
+// or from logits_in, fp64 softmax statistics, natural top-k (written in slot
+// order), demand terms into sm.c[slot], anchor / natural-use flags, error
+// bits.  d, p, dp, cf: depth, parent, parent's depth and commit[depth] of
+// node i.
+template <int Q, int NPW>
+__device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
+                                           NodeSmem<NPW>& sm, int d, int p, int dp, float cf,
+                                           const float* bias, const float* lrow) {
   const int lane = lane_id();
   const int E = a.E, k = a.k;
   const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
@@ -172,6 +187,13 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
       const int e = lane + kWave * q;
       valid[q] = e < E;
       l[q] = valid[q] ? a.logits_in[static_cast<size_t>(i) * E + e] : 0.f;
+    }
+  } else if (lrow) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      valid[q] = e < E;
+      l[q] = valid[q] ? lrow[e] + bias[q] : 0.f;
     }
   } else {
     // K-slice partial sums: every load issued first, then summed in slice order
@@ -299,8 +321,8 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
 // note any count outside its range in counters[0].  A nonzero counter here
 // means the workspace was not zero-filled before its first use, or was
 // shared by calls that overlap: the call's outputs are then flagged
-// (kErrWorkspace), and the counters are set back to zero so that the
-// restricted kernel of this call and later calls elect correctly.  The tail
+// (kErrWorkspace), and the counters are set back to zero so that later
+// calls elect correctly (counters[1] is reserved and must be zero).  The tail
 // kernel's threads load the nwg + 2 counters (counters[0..1], then the node
 // groups' gcount) with the kernel's other first loads; select_set checks and
 // repairs them.
@@ -744,19 +766,20 @@ __device__ __forceinline__ void node_deps(const SelectArgs& a, int node, int d, 
 // together.  The node's dependent inputs (commit of
 // its depth, its parent's depth) are loaded once the product's loads are
 // out, so that they share the round trip.
-template <typename AT, int TPW>
+template <typename AT, int TPW, int NPW>
 __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int ks, int wave,
                                                 int lane, int node, int d, int p, float& cf,
-                                                int& dp) {
+                                                int& dp, float (*lds)[kMaxE]) {
   constexpr int S = RouterSteps<AT>::n;
   const int N = a.N, E = a.E, H = a.H;
-  const int n0 = g * kNodesPerWG;
+  const int n0 = g * NPW;
   const int kbeg = ks * a.kslice;
   const int nsteps = min(H - kbeg, a.kslice) >> 5;
   const int mrow = lane & 15, kq = (lane >> 4) * 8;
-  // MFMA rows 4..15 repeat rows 0..3 (their D rows are never stored)
+  // NPW = 4: MFMA rows 4..15 repeat rows 0..3 (their D rows are never
+  // stored); NPW = 16: every row is a node
   const AT* xrow = static_cast<const AT*>(a.x) +
-                   static_cast<size_t>(min(n0 + (mrow & (kNodesPerWG - 1)), N - 1)) * H + kbeg + kq;
+                   static_cast<size_t>(min(n0 + (mrow & (NPW - 1)), N - 1)) * H + kbeg + kq;
   const AT* wrow[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -775,7 +798,7 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
       for (int s = 0; s < S; ++s) bf[tt][s].load(wrow[tt] + 32 * min(s0 + s, nsteps - 1));
 #pragma unroll
     for (int s = 0; s < S; ++s) af[s].load(xrow + 32 * min(s0 + s, nsteps - 1));
-    if (s0 == 0) {
+    if (NPW == kNodesPerWG && s0 == 0) {
       asm volatile("" ::: "memory");
       node_deps(a, node, d, p, cf, dp);
     }
@@ -786,78 +809,102 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
         for (int tt = 0; tt < TPW; ++tt) acc[tt] = rmma(af[s], bf[tt][s], acc[tt]);
       }
   }
-  // D rows 0..3 (the nodes) sit in lanes 0..15, one expert column each
-  if (lane < 16) {
+  // D rows 4gq..4gq+3 sit in lanes 16gq..16gq+15, one expert column each
+  // (NPW = 4: only rows 0..3, lanes 0..15, are nodes); into LDS when this
+  // work-group takes all of K, else to the partials at device scope
+  const int gq = lane >> 4;
+  if (NPW > kNodesPerWG || gq == 0) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      const int e = (wave + 4 * tt) * 16 + lane;
+      const int e = (wave + 4 * tt) * 16 + (lane & 15);
       if (e < E) {
 #pragma unroll
-        for (int r = 0; r < kNodesPerWG; ++r)
-          if (n0 + r < N) store_dev(a.part + (static_cast<size_t>(ks) * N + n0 + r) * E + e, acc[tt][r]);
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * gq + j;
+          if (lds)
+            lds[r][e] = acc[tt][j];
+          else if (n0 + r < N)
+            store_dev(a.part + (static_cast<size_t>(ks) * N + n0 + r) * E + e, acc[tt][j]);
+        }
       }
     }
   }
 }
 
 // ------------------------------------------------------------- kernel ----
-// Q: 64-expert slots per lane, ceil(E / 64)
-template <typename AT, int Q>
+// Q: 64-expert slots per lane, ceil(E / 64); NPW nodes per group (wave w
+// takes nodes n0 + w, n0 + w + 4, ... in the node phase)
+template <typename AT, int Q, int NPW>
 __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
-  __shared__ NodeSmem sm;
+  constexpr int PER_WAVE = NPW / 4;
+  __shared__ NodeSmem<NPW> sm;
   const int t = threadIdx.x, wave = t >> 6, lane = lane_id();
   const int g = blockIdx.x, ks = blockIdx.y;
   const int N = a.N, E = a.E;
-  const int n0 = g * kNodesPerWG;
-  const int node = n0 + wave;  // this wave's node in the node phase
-  const bool has_node = node < N;
+  const int n0 = g * NPW;
   const bool logits_in = (a.flags & kFlagLogitsIn) != 0;
+  // one work-group takes all of K (NPW > 4 only): the logits stay in LDS
+  const bool whole_k = NPW > kNodesPerWG && gridDim.y == 1;
 
   // node-phase inputs that do not depend on the logits, loaded up front (from
   // clamped addresses, without branches) so that their latency hides under
   // the router phase; the dependent ones follow once the product's loads are
   // out
-  const int nd = min(node, N - 1);
-  const int d = a.depth[nd], p = a.parent[nd];
+  int d[PER_WAVE], p[PER_WAVE], dp[PER_WAVE];
+  float cf[PER_WAVE];
+#pragma unroll
+  for (int s = 0; s < PER_WAVE; ++s) {
+    const int nd = min(n0 + wave + 4 * s, N - 1);
+    d[s] = a.depth[nd];
+    p[s] = a.parent[nd];
+  }
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.b_router) {
 #pragma unroll
     for (int q = 0; q < Q; ++q) bias[q] = a.b_router[min(lane + kWave * q, E - 1)];
   }
-  float cf;
-  int dp;
   if (!logits_in) {
-    // ---- partial logits of the group's 4 nodes over K slice ks
+    // ---- partial logits of the group's nodes over K slice ks
     const int tpw = ((E + 15) / 16 + 3) / 4;  // 16-expert tiles per wave
+    float (*lds)[kMaxE] = whole_k ? sm.lg : nullptr;
+    const int node = n0 + wave;
     if (tpw == 1)
-      router_partials<AT, 1>(a, g, ks, wave, lane, node, d, p, cf, dp);
+      router_partials<AT, 1, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
     else if (tpw == 2)
-      router_partials<AT, 2>(a, g, ks, wave, lane, node, d, p, cf, dp);
+      router_partials<AT, 2, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
     else if (tpw == 3)
-      router_partials<AT, 3>(a, g, ks, wave, lane, node, d, p, cf, dp);
+      router_partials<AT, 3, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
     else
-      router_partials<AT, 4>(a, g, ks, wave, lane, node, d, p, cf, dp);
+      router_partials<AT, 4, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
     // partials travel at device scope: no cache write-back or invalidation
-    if (!last_arrival_dev(&a.gcount[g], gridDim.y, &a.counters[0])) return;
-  } else {
-    node_deps(a, node, d, p, cf, dp);
+    if (!whole_k && !last_arrival_dev(&a.gcount[g], gridDim.y, &a.counters[0])) return;
+  }
+  if (logits_in || NPW > kNodesPerWG) {
+#pragma unroll
+    for (int s = 0; s < PER_WAVE; ++s) node_deps(a, n0 + wave + 4 * s, d[s], p[s], cf[s], dp[s]);
   }
 
   // ---- node phase (the group's last K-slice work-group)
   for (int x = t; x < kMaxE; x += 256) {
     sm.flags[x] = 0;
 #pragma unroll
-    for (int w = 0; w < kNodesPerWG; ++w) sm.c[w][x] = 0.0;
+    for (int w = 0; w < NPW; ++w) sm.c[w][x] = 0.0;
   }
   if (t == 0) sm.err = 0;
   __syncthreads();
-  if (has_node) node_phase<Q>(a, node, wave, sm, d, p, dp, cf, bias);
+#pragma unroll
+  for (int s = 0; s < PER_WAVE; ++s) {
+    const int slot = wave + 4 * s;
+    if (n0 + slot < N)
+      node_phase<Q, NPW>(a, n0 + slot, slot, sm, d[s], p[s], dp[s], cf[s], bias,
+                         whole_k && !logits_in ? sm.lg[slot] : nullptr);
+  }
   __syncthreads();
   const int ds = dpart_stride(N), fs = fpart_stride(N);
   for (int x = t; x < E; x += 256) {
     double dsum = 0.0;
 #pragma unroll
-    for (int w = 0; w < kNodesPerWG; ++w) dsum += sm.c[w][x];  // node order
+    for (int w = 0; w < NPW; ++w) dsum += sm.c[w][x];  // node order
     a.d_part[static_cast<size_t>(x) * ds + g] = dsum;
     a.f_part[static_cast<size_t>(x) * fs + g] = static_cast<uint8_t>(sm.flags[x]);
   }
@@ -929,7 +976,6 @@ __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
 
 // one wave per node, 4 nodes per work-group (N > kFusedMaxN)
 __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
-  __shared__ PermuteSmem<256> perm;
   const int lane = lane_id();
   const int i = blockIdx.x * kNodesPerWG + static_cast<int>(threadIdx.x >> 6);
   if (i < a.N) {
@@ -991,17 +1037,21 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
       a.topk_gate[static_cast<size_t>(i) * k + lane] = static_cast<float>(g);
     }
   }
-  // the last work-group to finish groups the assignments by expert, or
-  // (without the grouping) counts the active experts for the statistics
+}
+
+// After restricted_kernel (N > kFusedMaxN): one work-group of kTail threads
+// groups the N*k assignments by expert (N*k / kTail rounds of the ballot
+// ranking), or, without the grouping, counts the active experts for the
+// statistics.
+__global__ __launch_bounds__(kTail) void group_kernel(SelectArgs a) {
+  __shared__ PermuteSmem<kTail> perm;
   StatsDev* st = static_cast<StatsDev*>(a.stats);
-  if (last_block_done(&a.counters[1], gridDim.x, &st->err_flags)) {
-    if (a.counts)
-      permute_block<256>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
+  if (a.counts)
+    permute_block<kTail>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
                          a.inv_pos, a.active, a.n_active, a.resident, st, perm, a.max_rows,
                          a.groups, a.active_w);
-    else
-      active_stats<256>(a.N * a.k, a.E, a.topk_idx, a.resident, st, perm.cnt);
-  }
+  else
+    active_stats<kTail>(a.N * a.k, a.E, a.topk_idx, a.resident, st, perm.cnt);
 }
 
 }  // namespace
@@ -1009,7 +1059,7 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
 void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) {
   // about 128 work-groups (groups x K slices), at most kMaxKSplit slices of
   // at most kMaxSlice elements each, multiples of 64
-  const int groups = (N + kNodesPerWG - 1) / kNodesPerWG;
+  const int groups = node_groups(N);
   int ks = (128 + groups - 1) / groups;
   if (ks > kMaxKSplit) ks = kMaxKSplit;
   const int min_ks = (H + kMaxSlice - 1) / kMaxSlice;
@@ -1026,31 +1076,39 @@ int node_workgroups(int N) { return node_groups(N); }
 size_t dpart_elems(int N, int E) { return static_cast<size_t>(dpart_stride(N)) * E; }
 size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N)) * E; }
 
+template <typename AT, int NPW>
+void launch_front(const SelectArgs& a, dim3 grid, int q, hipStream_t stream) {
+  if (q == 1)
+    front_kernel<AT, 1, NPW><<<grid, 256, 0, stream>>>(a);
+  else if (q == 2)
+    front_kernel<AT, 2, NPW><<<grid, 256, 0, stream>>>(a);
+  else if (q == 3)
+    front_kernel<AT, 3, NPW><<<grid, 256, 0, stream>>>(a);
+  else
+    front_kernel<AT, 4, NPW><<<grid, 256, 0, stream>>>(a);
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const bool lin = (a.flags & kFlagLogitsIn) != 0;
   const dim3 grid(node_groups(a.N), lin ? 1 : a.ksplit, 1);
   const int q = (a.E + kWave - 1) / kWave;
+  const bool big = nodes_per_group(a.N) == kNodesPerWGBig;
   if (a.act_bf16) {
-    if (q == 1)
-      front_kernel<uint16_t, 1><<<grid, 256, 0, stream>>>(a);
-    else if (q == 2)
-      front_kernel<uint16_t, 2><<<grid, 256, 0, stream>>>(a);
-    else if (q == 3)
-      front_kernel<uint16_t, 3><<<grid, 256, 0, stream>>>(a);
+    if (big)
+      launch_front<uint16_t, kNodesPerWGBig>(a, grid, q, stream);
     else
-      front_kernel<uint16_t, 4><<<grid, 256, 0, stream>>>(a);
+      launch_front<uint16_t, kNodesPerWG>(a, grid, q, stream);
   } else {
-    if (q == 1)
-      front_kernel<float, 1><<<grid, 256, 0, stream>>>(a);
-    else if (q == 2)
-      front_kernel<float, 2><<<grid, 256, 0, stream>>>(a);
-    else if (q == 3)
-      front_kernel<float, 3><<<grid, 256, 0, stream>>>(a);
+    if (big)
+      launch_front<float, kNodesPerWGBig>(a, grid, q, stream);
     else
-      front_kernel<float, 4><<<grid, 256, 0, stream>>>(a);
+      launch_front<float, kNodesPerWG>(a, grid, q, stream);
   }
   tail_kernel<<<1, kTail, 0, stream>>>(a);
-  if (a.N > kFusedMaxN) restricted_kernel<<<node_groups(a.N), 256, 0, stream>>>(a);
+  if (a.N > kFusedMaxN) {
+    restricted_kernel<<<(a.N + kNodesPerWG - 1) / kNodesPerWG, 256, 0, stream>>>(a);
+    group_kernel<<<1, kTail, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
