@@ -56,6 +56,7 @@ struct SelectArgs {
   int32_t* max_rows;  // or null: the most rows routed to one expert
   int32_t* groups;    // or null: the active experts' 64-row groups (see permute_block)
   int32_t* active_w;  // or null: the active experts in work order (see permute_block)
+  int group_shift;    // the groups table lists (1 << group_shift)-row groups (6 or 7)
 };
 
 // router product, per-node softmax / natural top-k / demand terms, set
@@ -116,6 +117,10 @@ struct GroupedArgs {
   // see permute_block): a grid of whole rounds of one work-group per CU
   // deals the items in a snake over the rounds
   int snake;
+  // packed bf16 / fp8: GEMM tiling for many rows per expert (two 64-row
+  // items per work-group, up to 128 routed rows a pass; the groups table, if
+  // used, then lists 128-row groups)
+  int gemm;
   // bf16 / fp8, when > 0: dense mode -- dense_n experts (active[0..dense_n),
   // or 0..dense_n-1 when active is null; offsets, sorted_assign and
   // n_active unused) each over all N rows: row m of expert u is node m's x,

@@ -75,7 +75,8 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
                                               const uint8_t* resident, StatsDev* stats,
                                               PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
                                               int32_t* groups = nullptr,
-                                              int32_t* active_w = nullptr) {
+                                              int32_t* active_w = nullptr,
+                                              int group_shift = 6) {
   constexpr int NW = NTHR / kWave;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
@@ -90,7 +91,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   if (t < E) {
     const int c = sm.cnt[t];
     sm.flag[t] = c > 0 ? 1 : 0;
-    sm.ng[t] = (c + 63) >> 6;
+    sm.ng[t] = (c + (1 << group_shift) - 1) >> group_shift;
     // cost class of the expert's work items (activation rows staged per
     // chunk: 64 / 32 / 16), one 10-bit count field each
     sm.cls[t] = c > 32 ? 1 : (c > 16 ? (1 << 10) : (c > 0 ? (1 << 20) : 0));
@@ -122,7 +123,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     }
     sm.wpos[t] = wp;
   }
-  // the 64-row groups of the active experts in work order, as
+  // the (1 << group_shift)-row groups of the active experts, as
   // (work index << 16 | group): groups[0] = count, groups[1 + g] = entry g
   // (thread t reads only the work position it wrote)
   if (groups) {

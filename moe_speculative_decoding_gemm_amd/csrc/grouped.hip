@@ -416,11 +416,22 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const u32x2_t& u) {
   return f;
 }
 
-// FP8: two resident work-groups per CU (the register budget is cut to fit)
-template <int WK, bool GATEUP, int NT, int KC, bool PACKED>
-__global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(GroupedArgs a) {
+// FP8: two resident work-groups per CU (the register budget is cut to fit),
+// except with paired items.
+//
+// GEMM tiling for blocks with many rows per expert (PAIRED, MTMAX = 8): a
+// work-group takes two adjacent 64-row items of the packed layout (wave w:
+// tile w of each, 32 weight rows per wave) against up to 128 routed rows at
+// a time, so every staged activation chunk feeds twice the weight rows and
+// every weight chunk twice the routed rows of the default tiling -- a
+// quarter of the bytes per MFMA operation moved through the CU.  Each
+// output element is accumulated by the same MFMA sequence as in the default
+// tiling, so the results are the same bits.
+template <int WK, bool GATEUP, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false>
+__global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_kernel(GroupedArgs a) {
   static_assert(!PACKED || KC == kPackChunk, "packed weights come in 128-long chunks");
-  constexpr int MT = 4;
+  static_assert(!PAIRED || (PACKED && NT == 2), "paired items: packed weights, two tiles a wave");
+  constexpr int MT = MTMAX;
   constexpr int ROWS = 16 * MT;
   constexpr int STEPS = KC / 32;
   constexpr int LDK = KC + 8;         // LDS row stride in bf16 elements (16 B pad)
@@ -497,7 +508,8 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
     int half = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int q = (tile * 4 + wave) * NT + nt;  // 16-row tile index within the expert
+      // 16-row tile index within the expert
+      const int q = PAIRED ? (2 * tile + nt) * 4 + wave : (tile * 4 + wave) * NT + nt;
       if (GATEUP) {
         half = r >> 3;
         const int irow = q * 8 + (r & 7);
@@ -513,10 +525,15 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
     }
     const float* scales = GATEUP ? a.s13 : a.s2;
     const int nkb = K >> 7;
-    // packed: this wave's fragments of the item, chunk-major (see pack_kernel)
+    // packed: this wave's fragments of the item, chunk-major (see pack_kernel);
+    // paired: of the first of the two items (NT = 1 layout), the second one
+    // item_stride elements further
+    constexpr int PNT = PAIRED ? 1 : NT;  // tiles per wave in the packed layout
+    const size_t item_stride = static_cast<size_t>(nchunks) * 16 * kFragElems;
     const WTp* pbase = static_cast<const WTp*>(GATEUP ? a.w13 : a.w2) +
-                       (static_cast<size_t>(ew) * tiles + tile) * nchunks * (16 * NT) * kFragElems +
-                       static_cast<size_t>(wave) * NT * kFragElems + lane * 8;
+                       (static_cast<size_t>(ew) * tiles * (NT / PNT) + tile * (NT / PNT)) *
+                           nchunks * (16 * PNT) * kFragElems +
+                       static_cast<size_t>(wave) * PNT * kFragElems + lane * 8;
 
     for (int mg = g0 * ROWS; mg < te; mg += rstep * ROWS) {
       // One group of routed rows mg.. with MTV 16-row M tiles: only as many
@@ -582,10 +599,11 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
 #pragma unroll
           for (int j = 0; j < STEPS; ++j) {
             if (PACKED) {
-              const WTp* f = pbase + static_cast<size_t>((min(c, nchunks - 1) * 4 + j) * 4 * NT) * kFragElems;
+              const WTp* f = pbase + static_cast<size_t>((min(c, nchunks - 1) * 4 + j) * 4 * PNT) * kFragElems;
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt)
-                b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(f + nt * kFragElems));
+                b[j][nt] = __builtin_nontemporal_load(reinterpret_cast<const BR*>(
+                    f + (PAIRED ? nt * item_stride : static_cast<size_t>(nt) * kFragElems)));
             } else {
               const int s = min(c * STEPS + j, nsteps - 1);
 #pragma unroll
@@ -633,8 +651,9 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         };
 
         // Weight chunks in flight: 2 for bf16, 4 for fp8 (an fp8 chunk is half
-        // the bytes; a CU streams at the rate its bytes in flight allow).
-        constexpr int DW = WK == 2 ? 4 : 2;
+        // the bytes; a CU streams at the rate its bytes in flight allow); 2
+        // for paired items, which already carry two tiles a wave.
+        constexpr int DW = (WK == 2 && !PAIRED) ? 4 : 2;
         BR bq[DW][STEPS][NT];
         float bsc[DW][NT];  // FP8 block scales of the chunks in flight
         // prologue: A0 B0 A1 B1 .. B(DW-1)
@@ -647,7 +666,7 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         // behind the pipeline's loads and used only by the epilogue
         const bool tok = !GATEUP && a.tok_rows && !dense;
         int my_row = 0;
-        if (tok) my_row = a.sorted_assign[off + min(mg + lane, te - 1)];
+        if (tok && t < ROWS) my_row = a.sorted_assign[off + min(mg + t, te - 1)];
         stage_store(sv[0], 0);
         __syncthreads();
         // chunk c: weights in ring slot c % DW, activations in VGPR ring / LDS
@@ -699,12 +718,15 @@ __global__ __launch_bounds__(256, WK == 2 ? 2 : 1) void expert_lds_kernel(Groupe
         }
       };
       const int rows = te - mg;
-      if (rows <= 16)
+      if (rows <= 16) {
         group(std::integral_constant<int, 1>{});
-      else if (rows <= 32)
+      } else if (rows <= 32) {
         group(std::integral_constant<int, 2>{});
-      else
+      } else if (MTMAX <= 4 || rows <= 64) {
         group(std::integral_constant<int, 4>{});
+      } else {
+        if constexpr (MTMAX >= 8) group(std::integral_constant<int, 8>{});
+      }
     }
   }
 }
@@ -793,21 +815,23 @@ int resident_per_cu(Kern kern, int fallback) {
   return n;
 }
 
-template <int WK, int NT, int KC, bool PACKED>
+template <int WK, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false>
 void launch_lds(const GroupedArgs& a, hipStream_t stream, int which) {
-  static const int occ_g = resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED>, 2);
-  static const int occ_d = resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED>, 2);
+  static const int occ_g =
+      resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED>, 2);
+  static const int occ_d =
+      resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED>, 2);
   const int max_active = a.dense_n > 0 ? a.dense_n : (a.E < a.N * a.k ? a.E : a.N * a.k);
   const int R = a.row_groups > 1 ? a.row_groups : 1;
   if (which != 2) {
     const int items = max_active * (2 * a.I / (64 * NT)) * R;
     const int grid = items < occ_g * a.num_cu ? items : occ_g * a.num_cu;
-    expert_lds_kernel<WK, true, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
+    expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED><<<grid, 256, 0, stream>>>(a);
   }
   if (which != 1) {
     const int items = max_active * (a.H / (64 * NT)) * R;
     const int grid = items < occ_d * a.num_cu ? items : occ_d * a.num_cu;
-    expert_lds_kernel<WK, false, NT, KC, PACKED><<<grid, 256, 0, stream>>>(a);
+    expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED><<<grid, 256, 0, stream>>>(a);
   }
 }
 
@@ -817,13 +841,17 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which) {
       launch_wk<0>(a, stream, which);
       break;
     case 1:
-      if (a.packed)
+      if (a.packed && a.gemm)
+        launch_lds<1, 2, kPackChunk, true, 8, true>(a, stream, which);
+      else if (a.packed)
         launch_lds<1, kPackNT_bf16, kPackChunk, true>(a, stream, which);
       else
         launch_lds<1, 1, 128, false>(a, stream, which);
       break;
     default:
-      if (a.packed)
+      if (a.packed && a.gemm)
+        launch_lds<2, 2, kPackChunk, true, 8, true>(a, stream, which);
+      else if (a.packed)
         launch_lds<2, kPackNT_fp8, kPackChunk, true>(a, stream, which);
       else
         launch_lds<2, 1, 128, false>(a, stream, which);

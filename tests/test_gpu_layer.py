@@ -67,6 +67,11 @@ SMALL = [
     # separate units next to each other
     ("qwen3_30b", dict(E=12, k=4, H=256, I=320, N=300)),
     ("dsv31", dict(E=10, k=3, H=256, I=256, N=200, n_chains=25, chain_len=8)),
+    # 256 or more routed rows per expert on average, packed weights: the
+    # GEMM tiling (two 64-row items per work-group, 128-row groups), fp8 with
+    # the shared expert, bf16 with an odd number of 64-row items per expert
+    ("dsv31", dict(E=10, k=3, H=256, I=256, N=1000, n_chains=125, chain_len=8)),
+    ("qwen3_30b", dict(E=24, k=4, H=384, I=320, N=1560)),
     # the largest sizes: 4096 nodes (thousands of rows per expert, dozens of
     # 64-row groups each), and 256 experts with top-16
     ("qwen3_30b", dict(E=16, k=8, H=128, I=128, N=4096)),
