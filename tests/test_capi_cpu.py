@@ -189,3 +189,26 @@ def test_noalloc_rejects_a_block_beyond_its_workspace(m):
     sh64 = _shape(m)
     assert m.acceptmoe_workspace_size(sh64) <= m.NOALLOC_WORKSPACE_BYTES
     assert lib.verify_block_noalloc(C.byref(sh64), None, C.byref(out), None) == m.EINVAL
+
+
+def test_overlap_argument_checks(m):
+    """verify_block_overlap refuses a missing side stream or event, and a side
+    stream equal to the call's stream, before anything is enqueued."""
+    lib = m.raw()
+    sh = _shape(m, w_layout=m.LAYOUT_PACKED)
+    inp = m.Inputs(*([FAKE.value] * 16))
+    out = m.Outputs(*([FAKE.value] * 8))
+    ws_bytes = m.acceptmoe_workspace_size(sh)
+    stream = C.c_void_p(0x2000)
+    ok = m.Overlap(0x3000, 0x4000, 0x5000)
+    cases = [None, m.Overlap(None, 0x4000, 0x5000), m.Overlap(0x3000, None, 0x5000),
+             m.Overlap(0x3000, 0x4000, None), m.Overlap(0x2000, 0x4000, 0x5000)]
+    for ov in cases:
+        ref = C.byref(ov) if ov is not None else None
+        rc = lib.verify_block_overlap(C.byref(sh), C.byref(inp), C.byref(out), ref, FAKE,
+                                      ws_bytes, stream)
+        assert rc == m.EINVAL, ov
+    # a valid overlap descriptor still fails the workspace check first
+    rc = lib.verify_block_overlap(C.byref(sh), C.byref(inp), C.byref(out), C.byref(ok), FAKE,
+                                  ws_bytes - 1, stream)
+    assert rc == m.EINVAL and b"workspace" in lib.acceptmoe_last_error()

@@ -57,3 +57,51 @@ def test_noalloc_matches_verify_block(lib):
         err = max_rel_err(got["y"], oref["y"])
         say(f"  U={U} rel err {err:.2e}")
         assert err <= TOL[cfg.w]
+
+
+def test_noalloc_graph_replays(lib):
+    """verify_block_noalloc captured in a HIP graph (its counter clear is a
+    kernel, not a memset node): every replay, with eager work between the
+    replays, gives the bits verify_block gives."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=48, k=8, H=512, I=384, N=64)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    blocks = [W.make_block(cfg, s) for s in range(2)]
+    sh = shape_of(lib, cfg)
+    ws = torch.zeros(lib.acceptmoe_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    ins, refs, outs = [], [], []
+    for b in blocks:
+        d = upload_block(b)
+        inputs = dict(x=d["x"], w_router=d["w_router"], b_router=d["b_router"],
+                      parent=d["parent"], depth=d["depth"], commit=d["commit"],
+                      resident=d["resident"], w13=w["w13"], w2=w["w2"])
+        ref = outputs_like(lib, cfg)
+        lib.verify_block(sh, inputs, ref, ws)
+        ins.append(inputs)
+        refs.append(ref)
+        outs.append(outputs_like(lib, cfg))
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for inputs, o in zip(ins, outs):
+            lib.verify_block_noalloc(sh, inputs, o)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graphs = []
+    for inputs, o in zip(ins, outs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lib.verify_block_noalloc(sh, inputs, o)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    junk = torch.empty(1 << 20, device="cuda")
+    for rep in range(3):
+        for i, g in enumerate(graphs):
+            junk.normal_()
+            for key in KEYS:
+                outs[i][key].zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            say(f"noalloc graph replay {rep} block {i}")
+            for key in KEYS:
+                assert torch.equal(outs[i][key], refs[i][key]), f"replay {rep} block {i}: {key}"
