@@ -26,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libacceptmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["select.hip", "permute.hip", "grouped.hip", "capi.cpp", "noalloc.hip"]
+SOURCES = ["select.hip", "permute.hip", "grouped.hip", "gemm.hip", "capi.cpp", "noalloc.hip"]
 
 # -packed-fp32-ops off: hipcc would otherwise emit packed fp32 adds/multiplies
 # on its own; the device code here is written for the unpacked forms.

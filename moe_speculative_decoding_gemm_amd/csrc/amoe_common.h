@@ -46,6 +46,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// SiLU of the SwiGLU experts [MoE-SD blog, MoE layer]: z * sigmoid(z)
+__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+
 template <typename T>
 __device__ __forceinline__ float load_act(const T* p, size_t i);
 template <>

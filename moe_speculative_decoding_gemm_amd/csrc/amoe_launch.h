@@ -56,7 +56,12 @@ struct SelectArgs {
   int32_t* max_rows;  // or null: the most rows routed to one expert
   int32_t* groups;    // or null: the active experts' 64-row groups (see permute_block)
   int32_t* active_w;  // or null: the active experts in work order (see permute_block)
-  int group_shift;    // the groups table lists (1 << group_shift)-row groups (6 or 7)
+  int group_shift;    // the groups table lists (1 << group_shift)-row groups (6 .. 8)
+  // when > 0: experts with more than split_rows routed rows go to the groups
+  // table as (1 << group_shift)-row groups for launch_gemm, the others to
+  // active_w, their number to n_work[0] (see permute_block)
+  int split_rows;
+  int32_t* n_work;
 };
 
 // router product, per-node softmax / natural top-k / demand terms, set
@@ -121,6 +126,10 @@ struct GroupedArgs {
   // items per work-group, up to 128 routed rows a pass; the groups table, if
   // used, then lists 128-row groups)
   int gemm;
+  // packed bf16: the groups table for launch_gemm (gemm_tile_rows()-row
+  // groups of the experts with more than 64 routed rows, (expert << 16) |
+  // group, see permute_block)
+  const int32_t* gemm_groups;
   // bf16 / fp8, when > 0: dense mode -- dense_n experts (active[0..dense_n),
   // or 0..dense_n-1 when active is null; offsets, sorted_assign and
   // n_active unused) each over all N rows: row m of expert u is node m's x,
@@ -129,6 +138,12 @@ struct GroupedArgs {
 };
 // which: 0 both projections, 1 gate/up only, 2 down only
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which = 0);
+
+// The tiled grouped GEMM (gemm.hip) over a.gemm_groups: packed bf16
+// weights only (gemm_supported).  which as above.
+bool gemm_supported(const GroupedArgs& a);
+int gemm_tile_rows();  // routed rows per GEMM tile (the groups table's group size)
+hipError_t launch_gemm(const GroupedArgs& a, hipStream_t stream, int which = 0);
 
 // Packed expert layout (bf16 / fp8 weights): see grouped.hip.  which: 0 for
 // w13 ([E,2,I,H] -> packed), 1 for w2 ([E,H,I] -> packed).

@@ -76,7 +76,8 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
                                               PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
                                               int32_t* groups = nullptr,
                                               int32_t* active_w = nullptr,
-                                              int group_shift = 6) {
+                                              int group_shift = 6, int split_rows = 0,
+                                              int32_t* n_work = nullptr) {
   constexpr int NW = NTHR / kWave;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
@@ -88,13 +89,16 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   __syncthreads();
   for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
   __syncthreads();
+  // split mode (split_rows > 0): an expert with more rows is "large"
+  const auto large = [&](int c) { return split_rows > 0 && c > split_rows; };
   if (t < E) {
     const int c = sm.cnt[t];
     sm.flag[t] = c > 0 ? 1 : 0;
-    sm.ng[t] = (c + (1 << group_shift) - 1) >> group_shift;
+    const int ng = (c + (1 << group_shift) - 1) >> group_shift;
+    sm.ng[t] = split_rows > 0 ? (large(c) ? ng : 0) : ng;
     // cost class of the expert's work items (activation rows staged per
-    // chunk: 64 / 32 / 16), one 10-bit count field each
-    sm.cls[t] = c > 32 ? 1 : (c > 16 ? (1 << 10) : (c > 0 ? (1 << 20) : 0));
+    // chunk: 64 / 32 / 16), one 10-bit count field each; none for a large one
+    sm.cls[t] = large(c) ? 0 : (c > 32 ? 1 : (c > 16 ? (1 << 10) : (c > 0 ? (1 << 20) : 0)));
   }
   __syncthreads();
   if (wave == 0) {
@@ -111,11 +115,12 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
   }
   __syncthreads();
   // work order: the active experts by cost class, the class that stages 64
-  // rows first, then 32, then 16, each class in index order; without
-  // active_w it is the active order
+  // rows first, then 32, then 16, each class in index order (in split mode
+  // the small experts only, their number in n_work[0]); without active_w it
+  // is the active order
   if (t < E) {
     int wp = sm.apos[t];
-    if (active_w && sm.flag[t]) {
+    if (active_w && sm.flag[t] && !large(sm.cnt[t])) {
       const int c = sm.cnt[t], cp = sm.cpos[t], ct = sm.ctot;
       const int n64 = ct & 1023, n32 = (ct >> 10) & 1023;
       wp = c > 32 ? (cp & 1023) : (c > 16 ? n64 + ((cp >> 10) & 1023) : n64 + n32 + (cp >> 20));
@@ -124,14 +129,20 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     sm.wpos[t] = wp;
   }
   // the (1 << group_shift)-row groups of the active experts, as
-  // (work index << 16 | group): groups[0] = count, groups[1 + g] = entry g
-  // (thread t reads only the work position it wrote)
+  // (work index << 16 | group), or in split mode the groups of the large
+  // experts, as (expert << 16 | group): groups[0] = count, groups[1 + g]
+  // = entry g (thread t reads only the work position it wrote)
   if (groups) {
     if (t < E) {
-      const int n = sm.ng[t], base = sm.gs[t], u = sm.wpos[t];
+      const int n = sm.ng[t], base = sm.gs[t];
+      const int u = split_rows > 0 ? t : sm.wpos[t];
       for (int j = 0; j < n; ++j) groups[1 + base + j] = (u << 16) | j;
     }
     if (t == 0) groups[0] = sm.ngrp;
+  }
+  if (n_work && active_w && t == 0) {
+    const int ct = sm.ctot;
+    n_work[0] = (ct & 1023) + ((ct >> 10) & 1023) + (ct >> 20);
   }
   if (t < E) {
     counts[t] = sm.cnt[t];

@@ -36,6 +36,8 @@ void timer_mark(int stage, bool begin, hipStream_t stream) {
 }
 
 constexpr int kMaxDevices = 64;
+// split mode starts where the experts average this many routed rows (N*k/E)
+constexpr int64_t kSplitRows = 64;
 std::atomic<int> g_num_cu[kMaxDevices];
 
 // compute units of the current device (queried once per device)
@@ -179,7 +181,9 @@ VerifyWs carve_verify(Carver& c, const acceptmoe_shape* s, bool shared) {
   w.sorted_assign = c.take<int32_t>(NK);
   w.inv_pos = c.take<int32_t>(NK);
   w.active = c.take<int32_t>(s->E);
-  w.n_active = c.take<int32_t>(2);  // [1]: the most rows routed to one expert
+  // [1]: the most rows routed to one expert; [2]: the small experts' count
+  // (split mode)
+  w.n_active = c.take<int32_t>(4);
   // 64-row groups of the active experts: at most N*k/64 + E, plus the count
   w.groups = c.take<int32_t>(2 + NK / 64 + s->E);
   // the active experts in the order the expert kernels take them
@@ -615,13 +619,11 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   // Qwen3-30B-shaped layer it pays from about that size on (N = 4096 natural
   // routing: 1292 -> 1191 us per block) and not below (N = 512 .. 2048:
   // 1-10 % slower).
-  const bool gemm = static_cast<int64_t>(s->N) * s->k >= 256ll * s->E &&
-                    s->w_layout == ACCEPTMOE_LAYOUT_PACKED && wk != 0 && !cache &&
-                    s->H % 128 == 0;
-  a.group_shift = gemm ? 7 : 6;
+  bool gemm = static_cast<int64_t>(s->N) * s->k >= 256ll * s->E &&
+              s->w_layout == ACCEPTMOE_LAYOUT_PACKED && wk != 0 && !cache &&
+              s->H % 128 == 0;
 
   amoe::GroupedArgs g = {};
-  g.gemm = gemm;
   g.N = s->N;
   g.k = s->k;
   g.E = s->E;
@@ -646,6 +648,17 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
   g.row_groups = 1;
   g.w_slot = cache ? cache->dev_expert_slot : nullptr;
   g.n_wslots = cache ? cache->state->n_slots + cache->state->n_spill : 0;
+  // Split mode (packed bf16 weights, blocks whose experts average kSplitRows
+  // routed rows or more): the experts with more than 64 routed rows run in
+  // the GEMM kernels (gemm.hip), the others in the streaming kernels.
+  const bool split = !cache && s->N > 64 &&
+                     static_cast<int64_t>(s->N) * s->k >= kSplitRows * s->E &&
+                     amoe::gemm_supported(g);
+  if (split) gemm = false;
+  g.gemm = gemm;
+  a.group_shift = split ? (amoe::gemm_tile_rows() == 128 ? 7 : 8) : (gemm ? 7 : 6);
+  a.split_rows = split ? 64 : 0;
+  a.n_work = w.n_active + 2;
 
   if (sh_side) {
     // the side stream starts after everything enqueued on `stream` before
@@ -708,6 +721,26 @@ int run_block(const acceptmoe_shape* s, const acceptmoe_inputs* in,
       rc = hip_status(amoe::launch_grouped(g, stream), "verify_block_cached/fetched expert");
       if (rc) return rc;
     }
+  } else if (split) {
+    // the large experts' row groups (GEMM), then the small experts
+    // (work order, at most 64 rows each: one row group per item)
+    amoe::GroupedArgs gs = g;
+    gs.gemm_groups = w.groups;
+    amoe::GroupedArgs gm = g;
+    gm.active = w.active_w;
+    gm.n_active = w.n_active + 2;
+    gm.groups = nullptr;
+    gm.max_rows = nullptr;
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
+    rc = hip_status(amoe::launch_gemm(gs, stream, 1), "verify_block/large experts gate-up");
+    if (!rc) rc = hip_status(amoe::launch_grouped(gm, stream, 1), "verify_block/experts gate-up");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_GATEUP, false, stream);
+    timer_mark(ACCEPTMOE_STAGE_DOWN, true, stream);
+    rc = hip_status(amoe::launch_gemm(gs, stream, 2), "verify_block/large experts down");
+    if (!rc) rc = hip_status(amoe::launch_grouped(gm, stream, 2), "verify_block/experts down");
+    if (rc) return rc;
+    timer_mark(ACCEPTMOE_STAGE_DOWN, false, stream);
   } else {
     timer_mark(ACCEPTMOE_STAGE_GATEUP, true, stream);
     rc = hip_status(amoe::launch_grouped(g, stream, 1), "verify_block/experts gate-up");

@@ -249,8 +249,6 @@ __device__ __forceinline__ void tile_product(const typename WeightT<WK>::T* wrow
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
-
 template <int WK>
 __global__ __launch_bounds__(256) void gateup_kernel(GroupedArgs a) {
   using WTp = typename WeightT<WK>::T;

@@ -739,7 +739,8 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
   if (a.counts)
     permute_block<kTail>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
                        a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
-                       sm.u.perm, a.max_rows, a.groups, a.active_w, a.group_shift);
+                       sm.u.perm, a.max_rows, a.groups, a.active_w, a.group_shift,
+                       a.split_rows, a.n_work);
   else
     active_stats<kTail>(NK, E, sm.top_e, a.resident, static_cast<StatsDev*>(a.stats),
                         sm.set.rank);
@@ -1049,7 +1050,7 @@ __global__ __launch_bounds__(kTail) void group_kernel(SelectArgs a) {
   if (a.counts)
     permute_block<kTail>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
                          a.inv_pos, a.active, a.n_active, a.resident, st, perm, a.max_rows,
-                         a.groups, a.active_w, a.group_shift);
+                         a.groups, a.active_w, a.group_shift, a.split_rows, a.n_work);
   else
     active_stats<kTail>(a.N * a.k, a.E, a.topk_idx, a.resident, st, perm.cnt);
 }

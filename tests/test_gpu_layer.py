@@ -328,3 +328,47 @@ def test_work_order_rounds_match_separate_path(lib, budget):
     say(f"  U={u} rows per active expert {sorted(rows.tolist(), reverse=True)}")
     assert u == st["n_active"] and rows.max() <= 64
     assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
+
+
+@pytest.mark.parametrize("over", [
+    # natural routing, ~500 rows per expert: every expert in the GEMM tiles,
+    # a partial last column tile (10 gate/up items), K = 320 padded to 384
+    dict(E=16, k=8, H=256, I=320, N=1024, flags=1),
+    # ~75 rows per expert on average: experts on both sides of 64 rows
+    dict(E=32, k=4, H=512, I=256, N=600),
+], ids=["all_large", "mixed"])
+def test_gemm_split_matches_separate_path(lib, over):
+    """Blocks whose experts average 64 or more routed rows (packed bf16): the
+    experts with more than 64 rows run in the 256 x 256-tile GEMM kernels,
+    the others in the streaming kernels.  The standalone grouped call runs
+    every expert in the streaming kernels; each output element takes the same
+    MFMA sequence in both, so y must be the same bits, and within the bf16
+    tolerance of the oracle."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(**over)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 5)
+    say(f"gemm split {over}")
+    out, st = run_layer(lib, cfg, b, w, pack=True)
+    ref = oracle_layer(cfg, b, w, out["logits_out"].cpu().numpy())
+    assert check_selection(out, ref, st, cfg, f"gemm split {over}")
+    assert max_rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+    N, H, I, E, k = cfg.N, cfg.H, cfg.I, cfg.E, cfg.k
+    dev = "cuda"
+    e_ = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
+    ti, tg = out["topk_idx"], out["topk_gate"]
+    counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)
+    lib.moe_route_permute(N, k, E, ti, counts, offsets, sa, ip, act, na)
+    w13, w2 = lib.pack_experts(shape_of(lib, cfg, w_layout=lib.LAYOUT_PACKED), w["w13"], w["w2"], E)
+    y_perm = e_(N * k, H, dt=torch.float32)
+    gws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, k, I, 1), dtype=torch.uint8,
+                      device=dev)
+    d = upload_block(b)
+    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 1, d["x"], w13, w2, None, None, offsets, sa, act,
+                           na, y_perm, gws, w_layout=lib.LAYOUT_PACKED)
+    y = e_(N, H, dt=torch.bfloat16)
+    lib.moe_combine(N, k, H, 1, y_perm, ip, tg, None, y)
+    torch.cuda.synchronize()
+    rows = counts.cpu().numpy()[act.cpu().numpy()[:int(na.item())]]
+    say(f"  U={int(na.item())} rows per active expert {sorted(rows.tolist(), reverse=True)}")
+    assert rows.max() > 64
+    assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
