@@ -43,8 +43,10 @@ struct SelectArgs {
   double* d_part;      // [E][groups, padded] demand summed over each 4-node group
   uint8_t* f_part;     // [E][groups, padded] bit 0: a root routes to the expert, bit 1: some node does
   int32_t* e_part;     // [groups] error bits of each node group
-  int32_t* counters;   // [2]: [0] arrivals seen outside their range, [1] reserved (zero)
+  int32_t* counters;   // [2]: [0] arrivals seen outside their range, [1] the grouping's
+                       // arrivals (N > 256; zero between kernels)
   int32_t* gcount;     // [N/4]: K-slice arrivals per node group (zero between calls)
+  int32_t* ghist;      // [ceil(N*k / 1024)][E]: per-chunk expert counts of the grouping (N > 256)
   // when non-null, the restricted top-k is followed by the grouping of the
   // assignments by expert (moe_route_permute's outputs)
   int32_t* counts;
@@ -69,6 +71,7 @@ struct SelectArgs {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 void select_plan(int N, int H, int E, int num_cu, int* ksplit, int* kslice);
 int node_workgroups(int N);  // node groups of the front kernel
+int group_chunks(int N, int k);  // chunks of the grouping for N > 256 (rows of ghist)
 size_t dpart_elems(int N, int E);  // doubles of d_part (expert-major rows of group partials)
 size_t fpart_bytes(int N, int E);  // bytes of f_part (same rows)
 

@@ -64,31 +64,21 @@ struct PermuteSmem {
   int nact, ngrp;
 };
 
-// Requires blockDim.x == NTHR (256 or 1024).  topk_idx may point to global
-// memory or to LDS.  An out-of-range expert id (a caller error) is clamped so
-// that no access leaves its buffer.
+// The tables of the grouping from the per-expert counts in sm.cnt[0..E)
+// (visible to the whole work-group): offsets, counts, the active list, the
+// work order, the row-group table, the largest count and the statistics.
+// Leaves the offsets in sm.off for permute_scatter.
 template <int NTHR>
-__device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t* topk_idx,
-                                              int32_t* counts, int32_t* offsets,
-                                              int32_t* sorted_assign, int32_t* inv_pos,
-                                              int32_t* active, int32_t* n_active,
-                                              const uint8_t* resident, StatsDev* stats,
-                                              PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
-                                              int32_t* groups = nullptr,
-                                              int32_t* active_w = nullptr,
-                                              int group_shift = 6, int split_rows = 0,
-                                              int32_t* n_work = nullptr) {
-  constexpr int NW = NTHR / kWave;
+__device__ __forceinline__ void permute_tables(int N, int k, int E, int32_t* counts,
+                                               int32_t* offsets, int32_t* active,
+                                               int32_t* n_active, const uint8_t* resident,
+                                               StatsDev* stats, PermuteSmem<NTHR>& sm,
+                                               int32_t* max_rows, int32_t* groups,
+                                               int32_t* active_w, int group_shift,
+                                               int split_rows, int32_t* n_work) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
   const int total = N * k;
-  if (t < kMaxE) {
-    sm.cnt[t] = 0;
-    sm.run[t] = 0;
-  }
-  __syncthreads();
-  for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
-  __syncthreads();
   // split mode (split_rows > 0): an expert with more rows is "large"
   const auto large = [&](int c) { return split_rows > 0 && c > split_rows; };
   if (t < E) {
@@ -169,10 +159,23 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
       stats->n_active_nonresident = nr;
     }
   }
+}
+
+// Pass 2 of the grouping over the assignments x0 .. x1-1: the first
+// assignment of expert e in the range goes to position sm.off[e] +
+// sm.run[e] (both set by the caller and visible to the whole work-group);
+// advances sm.run.
+template <int NTHR>
+__device__ __forceinline__ void permute_scatter(int x0, int x1, int E, const int32_t* topk_idx,
+                                                int32_t* sorted_assign, int32_t* inv_pos,
+                                                PermuteSmem<NTHR>& sm) {
+  constexpr int NW = NTHR / kWave;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = lane_id();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = 0; base < total; base += NTHR) {
+  for (int base = x0; base < x1; base += NTHR) {
     const int x = base + t;
-    const bool valid = x < total;
+    const bool valid = x < x1;
     const int e = valid ? clamp_expert(topk_idx[x], E) : 0;
     for (int q = lane; q < E; q += kWave) sm.w[wave][q] = 0;
     const uint64_t vmask = __ballot(valid);
@@ -188,7 +191,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     __syncthreads();
     if (t < E) {
       // only the waves that hold assignments in this round take part
-      const int nw = min(NW, (total - base + kWave - 1) / kWave);
+      const int nw = min(NW, (x1 - base + kWave - 1) / kWave);
       int run = sm.run[t];
       for (int w = 0; w < nw; ++w) {
         const int c = sm.w[w][t];
@@ -205,6 +208,34 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
     }
     __syncthreads();
   }
+}
+
+// Requires blockDim.x == NTHR (256 or 1024).  topk_idx may point to global
+// memory or to LDS.  An out-of-range expert id (a caller error) is clamped so
+// that no access leaves its buffer.
+template <int NTHR>
+__device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t* topk_idx,
+                                              int32_t* counts, int32_t* offsets,
+                                              int32_t* sorted_assign, int32_t* inv_pos,
+                                              int32_t* active, int32_t* n_active,
+                                              const uint8_t* resident, StatsDev* stats,
+                                              PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
+                                              int32_t* groups = nullptr,
+                                              int32_t* active_w = nullptr,
+                                              int group_shift = 6, int split_rows = 0,
+                                              int32_t* n_work = nullptr) {
+  const int t = threadIdx.x;
+  const int total = N * k;
+  if (t < kMaxE) {
+    sm.cnt[t] = 0;
+    sm.run[t] = 0;
+  }
+  __syncthreads();
+  for (int x = t; x < total; x += NTHR) atomicAdd(&sm.cnt[clamp_expert(topk_idx[x], E)], 1);
+  __syncthreads();
+  permute_tables<NTHR>(N, k, E, counts, offsets, active, n_active, resident, stats, sm, max_rows,
+                       groups, active_w, group_shift, split_rows, n_work);
+  permute_scatter<NTHR>(0, total, E, topk_idx, sorted_assign, inv_pos, sm);
 }
 
 }  // namespace amoe

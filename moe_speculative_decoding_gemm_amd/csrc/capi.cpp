@@ -37,7 +37,7 @@ void timer_mark(int stage, bool begin, hipStream_t stream) {
 
 constexpr int kMaxDevices = 64;
 // split mode starts where the experts average this many routed rows (N*k/E)
-constexpr int64_t kSplitRows = 64;
+constexpr int64_t kSplitRows = 32;
 std::atomic<int> g_num_cu[kMaxDevices];
 
 // compute units of the current device (queried once per device)
@@ -119,6 +119,7 @@ struct SelectWs {
   int32_t* e_part;
   int32_t* counters;
   int32_t* gcount;
+  int32_t* ghist;
   int ksplit, kslice;
 };
 
@@ -136,6 +137,7 @@ SelectWs carve_select(Carver& c, const acceptmoe_shape* s) {
   w.node_z = c.take<double>(s->N);
   w.nat_idx = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
   w.nat_logit = c.take<float>(static_cast<size_t>(s->N) * s->k);
+  w.ghist = c.take<int32_t>(static_cast<size_t>(amoe::group_chunks(s->N, s->k)) * s->E);
   const size_t nwg = amoe::node_workgroups(s->N);
   w.d_part = c.take<double>(amoe::dpart_elems(s->N, s->E));
   w.f_part = c.take<uint8_t>(amoe::fpart_bytes(s->N, s->E));
@@ -237,6 +239,7 @@ amoe::SelectArgs select_args(const acceptmoe_shape* s, const SelectWs& w) {
   a.e_part = w.e_part;
   a.counters = w.counters;
   a.gcount = w.gcount;
+  a.ghist = w.ghist;
   a.group_shift = 6;
   return a;
 }

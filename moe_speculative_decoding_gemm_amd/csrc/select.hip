@@ -322,7 +322,8 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
 // means the workspace was not zero-filled before its first use, or was
 // shared by calls that overlap: the call's outputs are then flagged
 // (kErrWorkspace), and the counters are set back to zero so that later
-// calls elect correctly (counters[1] is reserved and must be zero).  The tail
+// calls elect correctly (counters[1] counts the grouping's arrivals for
+// N > kFusedMaxN, after this kernel).  The tail
 // kernel's threads load the nwg + 2 counters (counters[0..1], then the node
 // groups' gcount) with the kernel's other first loads; select_set checks and
 // repairs them.
@@ -1040,19 +1041,74 @@ __global__ __launch_bounds__(256) void restricted_kernel(SelectArgs a) {
   }
 }
 
-// After restricted_kernel (N > kFusedMaxN): one work-group of kTail threads
-// groups the N*k assignments by expert (N*k / kTail rounds of the ballot
-// ranking), or, without the grouping, counts the active experts for the
-// statistics.
+// After restricted_kernel (N > kFusedMaxN), without the grouping: one
+// work-group counts the active experts for the statistics.
 __global__ __launch_bounds__(kTail) void group_kernel(SelectArgs a) {
   __shared__ PermuteSmem<kTail> perm;
+  active_stats<kTail>(a.N * a.k, a.E, a.topk_idx, a.resident, static_cast<StatsDev*>(a.stats),
+                      perm.cnt);
+}
+
+// After restricted_kernel (N > kFusedMaxN), with the grouping: the N*k
+// assignments in chunks of kGroupChunk, one work-group each.  Pass 1
+// (group_count_kernel): each chunk's expert counts go to ghist; the last
+// chunk to finish (elected on counters[1]) replaces them by each chunk's
+// first rank per expert (the counts of the chunks before it), and builds the
+// tables from the totals.  Pass 2 (group_scatter_kernel): each chunk places
+// its assignments from those ranks on.  Ranks follow assignment order, so
+// the grouping is the same stable sort as the one-work-group version.
+constexpr int kGroupChunk = kTail;
+
+__global__ __launch_bounds__(kTail) void group_count_kernel(SelectArgs a) {
+  __shared__ PermuteSmem<kTail> sm;
+  const int t = threadIdx.x, E = a.E, total = a.N * a.k;
+  const int C = static_cast<int>(gridDim.x);
+  const int x0 = static_cast<int>(blockIdx.x) * kGroupChunk;
+  const int x1 = min(total, x0 + kGroupChunk);
   StatsDev* st = static_cast<StatsDev*>(a.stats);
-  if (a.counts)
-    permute_block<kTail>(a.N, a.k, a.E, a.topk_idx, a.counts, a.offsets, a.sorted_assign,
-                         a.inv_pos, a.active, a.n_active, a.resident, st, perm, a.max_rows,
-                         a.groups, a.active_w, a.group_shift, a.split_rows, a.n_work);
-  else
-    active_stats<kTail>(a.N * a.k, a.E, a.topk_idx, a.resident, st, perm.cnt);
+  if (t < kMaxE) sm.cnt[t] = 0;
+  __syncthreads();
+  for (int x = x0 + t; x < x1; x += kTail) atomicAdd(&sm.cnt[clamp_expert(a.topk_idx[x], E)], 1);
+  __syncthreads();
+  if (t < E) store_dev(&a.ghist[static_cast<size_t>(blockIdx.x) * E + t], sm.cnt[t]);
+  // an arrival count out of range (a workspace that was not zero-filled or
+  // is shared by overlapping calls) is flagged in this call's statistics
+  if (!last_arrival_dev(&a.counters[1], C, &st->err_flags)) return;
+  // the chunks' counts, a batch of chunks at a time, loaded by every thread
+  // into LDS (sm.w is free here), then scanned over the chunks per expert
+  int* stage = &sm.w[0][0];
+  const int cb = static_cast<int>(sizeof(sm.w) / sizeof(int)) / E;  // chunks per batch
+  int run = 0;
+  for (int c0 = 0; c0 < C; c0 += cb) {
+    const int nc = min(cb, C - c0);
+    for (int i = t; i < nc * E; i += kTail)
+      stage[i] = load_dev(&a.ghist[static_cast<size_t>(c0) * E + i]);
+    __syncthreads();
+    if (t < E)
+      for (int c = 0; c < nc; ++c) {
+        const int n = stage[c * E + t];
+        a.ghist[static_cast<size_t>(c0 + c) * E + t] = run;
+        run += n;
+      }
+    __syncthreads();
+  }
+  if (t < E) sm.cnt[t] = run;
+  __syncthreads();
+  permute_tables<kTail>(a.N, a.k, E, a.counts, a.offsets, a.active, a.n_active, a.resident, st, sm,
+                        a.max_rows, a.groups, a.active_w, a.group_shift, a.split_rows, a.n_work);
+}
+
+__global__ __launch_bounds__(kTail) void group_scatter_kernel(SelectArgs a) {
+  __shared__ PermuteSmem<kTail> sm;
+  const int t = threadIdx.x, E = a.E, total = a.N * a.k;
+  const int x0 = static_cast<int>(blockIdx.x) * kGroupChunk;
+  const int x1 = min(total, x0 + kGroupChunk);
+  if (t < E) {
+    sm.off[t] = a.offsets[t];
+    sm.run[t] = a.ghist[static_cast<size_t>(blockIdx.x) * E + t];
+  }
+  __syncthreads();
+  permute_scatter<kTail>(x0, x1, E, a.topk_idx, a.sorted_assign, a.inv_pos, sm);
 }
 
 }  // namespace
@@ -1074,6 +1130,7 @@ void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) 
 }
 
 int node_workgroups(int N) { return node_groups(N); }
+int group_chunks(int N, int k) { return (N * k + kGroupChunk - 1) / kGroupChunk; }
 size_t dpart_elems(int N, int E) { return static_cast<size_t>(dpart_stride(N)) * E; }
 size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N)) * E; }
 
@@ -1108,7 +1165,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   tail_kernel<<<1, kTail, 0, stream>>>(a);
   if (a.N > kFusedMaxN) {
     restricted_kernel<<<(a.N + kNodesPerWG - 1) / kNodesPerWG, 256, 0, stream>>>(a);
-    group_kernel<<<1, kTail, 0, stream>>>(a);
+    if (a.counts) {
+      const int chunks = group_chunks(a.N, a.k);
+      group_count_kernel<<<chunks, kTail, 0, stream>>>(a);
+      group_scatter_kernel<<<chunks, kTail, 0, stream>>>(a);
+    } else {
+      group_kernel<<<1, kTail, 0, stream>>>(a);
+    }
   }
   return hipGetLastError();
 }
