@@ -59,9 +59,10 @@ struct SelectArgs {
   int32_t* groups;    // or null: the active experts' 64-row groups (see permute_block)
   int32_t* active_w;  // or null: the active experts in work order (see permute_block)
   int group_shift;    // the groups table lists (1 << group_shift)-row groups (6 .. 8)
-  // when > 0: experts with more than split_rows routed rows go to the groups
-  // table as (1 << group_shift)-row groups for launch_gemm, the others to
-  // active_w, their number to n_work[0] (see permute_block)
+  // when >= 0 (split mode): experts with more than split_rows routed rows go
+  // to the groups table as (1 << group_shift)-row groups for launch_gemm,
+  // the others to active_w, their number to n_work[0] (see permute_block);
+  // -1: off
   int split_rows;
   int32_t* n_work;
 };

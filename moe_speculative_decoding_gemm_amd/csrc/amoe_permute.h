@@ -79,13 +79,13 @@ __device__ __forceinline__ void permute_tables(int N, int k, int E, int32_t* cou
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = lane_id();
   const int total = N * k;
-  // split mode (split_rows > 0): an expert with more rows is "large"
-  const auto large = [&](int c) { return split_rows > 0 && c > split_rows; };
+  // split mode (split_rows >= 0): an expert with more rows is "large"
+  const auto large = [&](int c) { return split_rows >= 0 && c > split_rows; };
   if (t < E) {
     const int c = sm.cnt[t];
     sm.flag[t] = c > 0 ? 1 : 0;
     const int ng = (c + (1 << group_shift) - 1) >> group_shift;
-    sm.ng[t] = split_rows > 0 ? (large(c) ? ng : 0) : ng;
+    sm.ng[t] = split_rows >= 0 ? (large(c) ? ng : 0) : ng;
     // cost class of the expert's work items (activation rows staged per
     // chunk: 64 / 32 / 16), one 10-bit count field each; none for a large one
     sm.cls[t] = large(c) ? 0 : (c > 32 ? 1 : (c > 16 ? (1 << 10) : (c > 0 ? (1 << 20) : 0)));
@@ -125,7 +125,7 @@ __device__ __forceinline__ void permute_tables(int N, int k, int E, int32_t* cou
   if (groups) {
     if (t < E) {
       const int n = sm.ng[t], base = sm.gs[t];
-      const int u = split_rows > 0 ? t : sm.wpos[t];
+      const int u = split_rows >= 0 ? t : sm.wpos[t];
       for (int j = 0; j < n; ++j) groups[1 + base + j] = (u << 16) | j;
     }
     if (t == 0) groups[0] = sm.ngrp;
@@ -222,7 +222,7 @@ __device__ __forceinline__ void permute_block(int N, int k, int E, const int32_t
                                               PermuteSmem<NTHR>& sm, int32_t* max_rows = nullptr,
                                               int32_t* groups = nullptr,
                                               int32_t* active_w = nullptr,
-                                              int group_shift = 6, int split_rows = 0,
+                                              int group_shift = 6, int split_rows = -1,
                                               int32_t* n_work = nullptr) {
   const int t = threadIdx.x;
   const int total = N * k;

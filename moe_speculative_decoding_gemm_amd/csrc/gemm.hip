@@ -194,13 +194,16 @@ __global__ __launch_bounds__(256 * WR, 2 / WR) void gemm_kernel(GroupedArgs a) {
       u32x4_t av[8], bv[4];
       const uint32_t base = ring_base + (s % NS) * kSlot;
       read_frags(base + a_off, base + b_off, av, bv);
+      // only the row tiles that hold routed rows
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        if (i >= mt_n) break;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
                                                               __builtin_bit_cast(bf16x8_t, bv[q]),
                                                               acc[i][q], 0, 0, 0);
+      }
     };
     // Steps 0 .. NS-2 go out first; step s then waits for its own loads
     // (kLoads per wave: the loads of the up to NS-2 steps issued after it

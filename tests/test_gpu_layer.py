@@ -334,16 +334,20 @@ def test_work_order_rounds_match_separate_path(lib, budget):
     # natural routing, ~500 rows per expert: every expert in the GEMM tiles,
     # a partial last column tile (10 gate/up items), K = 320 padded to 384
     dict(E=16, k=8, H=256, I=320, N=1024, flags=1),
-    # ~75 rows per expert on average: experts on both sides of 64 rows
+    # ~75 rows per expert on average: every active expert in the GEMM tiles,
+    # also those with fewer than 64 rows (most row tiles empty)
     dict(E=32, k=4, H=512, I=256, N=600),
-], ids=["all_large", "mixed"])
+    # ~50 rows per expert on average: the experts with more than 64 rows in
+    # the GEMM tiles, the others in the streaming kernels
+    dict(E=32, k=4, H=512, I=256, N=400),
+], ids=["all_large", "all_gemm", "mixed"])
 def test_gemm_split_matches_separate_path(lib, over):
-    """Blocks whose experts average 64 or more routed rows (packed bf16): the
-    experts with more than 64 rows run in the 256 x 256-tile GEMM kernels,
-    the others in the streaming kernels.  The standalone grouped call runs
-    every expert in the streaming kernels; each output element takes the same
-    MFMA sequence in both, so y must be the same bits, and within the bf16
-    tolerance of the oracle."""
+    """Blocks whose experts average 32 or more routed rows (packed bf16): the
+    experts with many rows (from 64 mean rows on, every active expert) run in
+    the GEMM kernels, the others in the streaming kernels.  The standalone
+    grouped call runs every expert in the streaming kernels; each output
+    element takes the same MFMA sequence in both, so y must be the same bits,
+    and within the bf16 tolerance of the oracle."""
     cfg = W.CONFIGS["qwen3_30b"].with_(**over)
     w = make_weights(cfg, device="cuda", gen_device="cpu")
     b = W.make_block(cfg, 5)
