@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--moesd-sweep", action="store_true",
                     help="instead of the headline run: natural-routing layer time T(B, gamma) for "
                          "B sequences x gamma-token chains, and eta(B, gamma) = T(B,1)/T(B,gamma)")
+    ap.add_argument("--moesd-point", default=None, metavar="B,GAMMA",
+                    help="with --moesd-sweep: that one point only (e.g. 512,8 for N = 4096), "
+                         "for profiling")
     ap.add_argument("--budget-sweep", action="store_true",
                     help="fixed expert budget B = 8, 16, .., 128: us per block against active "
                          "experts U, with a least-squares line")
@@ -462,10 +465,13 @@ def moesd_sweep(args):
     points = []
     Bs = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
     gammas = [1, 2, 4, 8]
+    only = None
+    if args.moesd_point:
+        only = tuple(int(v) for v in args.moesd_point.split(","))
     for B in Bs:
         for gmm in gammas:
             N = B * gmm
-            if N > 4096:
+            if N > 4096 or (only is not None and (B, gmm) != only):
                 continue
             cfg = base.with_(N=N, n_chains=B, chain_len=gmm)
             layer = layer0.variant(N=N)
@@ -507,6 +513,8 @@ def moesd_sweep(args):
                            "U": statistics.mean(U), "U_uniform_model": round(u_model, 2)})
             log(f"B={B} gamma={gmm} N={N}: {t_us:.1f} us, U={statistics.mean(U):.1f} "
                 f"(uniform model {u_model:.1f})")
+    if only is not None and not points:
+        raise SystemExit(f"--moesd-point {args.moesd_point}: not a point of the sweep")
     t1 = {p["B"]: p["us"] for p in points if p["gamma"] == 1}
     for p in points:
         p["eta"] = round(t1[p["B"]] / p["us"], 4) if p["B"] in t1 else None
