@@ -47,7 +47,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // SiLU of the SwiGLU experts [MoE-SD blog, MoE layer]: z * sigmoid(z)
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+// (the hardware reciprocal, not a correctly rounded divide: every expert
+// kernel takes this same function, so all paths give the same bits)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ float load_act(const T* p, size_t i);

@@ -6,123 +6,137 @@
 // expert's FLOPs per weight byte grow with the batch until the layer turns
 // from memory-bound to compute-bound.  The streaming expert kernels
 // (grouped.hip) keep at most 128 routed rows per pass over an expert's
-// weights; here a work-group holds a 128 x 256 output tile -- 128 routed rows
-// of one expert against 256 weight rows (4 packed items) -- and two
-// work-groups share each CU (kWaveRows = 2: one 256 x 256 tile per CU).
+// weights; here one work-group per CU holds a 128 x 512 output tile -- 128
+// routed rows of one expert against 512 weight rows (8 packed items) -- in
+// 4 waves of 128 x 128 (8 x 8 MFMA tiles of 16 x 16, the accumulators in the
+// accumulation registers).
 //
-// Operands go from memory to LDS with gfx950's direct loads
-// (global_load_lds_dwordx4: 16 B per lane, no registers in between), already
-// in MFMA fragment order: one wave load instruction fills one 1 KB fragment
-// (lane l's 16 B at byte 16 l), so each fragment read is one conflict-free
-// ds_read_b128 per lane.  A ring of 32-long reduction steps (one slot: the
-// tile's activation fragments, then its 16 weight fragments) keeps NS - 1
-// steps in flight.
+// Every output element takes the same v_mfma_f32_16x16x32_bf16 sequence
+// over the same reduction steps (activation elements past K clamped the
+// same way) as in the streaming kernels, so the results are the same bits.
 //
-// Waves as kWaveRows x 4: wave (wm, wn) owns routed rows 128 wm .. +127 and
-// weight rows 64 wn .. +63 (one packed item) of the tile, 8 x 4 MFMA tiles of
-// 16 x 16.  Every output element takes the same v_mfma_f32_16x16x32_bf16
-// sequence over the same reduction steps (activation elements past K clamped
-// the same way) as in the streaming kernels, so the results are the same bits.
-//
-// Work units: (row group of an expert, 256-column tile), group-major, from
+// Work units: (row group of an expert, 512-column tile), group-major, from
 // the groups table that the grouping writes for these experts.  The grid
-// is every work-group slot of the GPU; work-group b runs on XCD b mod 8, so
-// XCD x takes the contiguous unit range x * span .. and its CUs work on
-// neighbouring units at the same time: the column tiles of one row group
-// share its activation rows, and the row groups of one expert share the
-// weights, in that XCD's L2.
+// is one work-group per CU; work-group b runs on XCD b mod 8, so XCD x takes
+// the contiguous unit range x * span .. and its CUs work on neighbouring
+// units at the same time: the column tiles of one row group share its
+// activation rows, and the row groups of one expert share the weights, in
+// that XCD's L2.
 
 #include "amoe_common.h"
 #include "amoe_launch.h"
+
+#include <type_traits>
 
 namespace amoe {
 
 namespace {
 
-constexpr int kTileItems = 4;                 // packed 64-row weight items per tile
 constexpr int kFragBytes = 1024;              // one MFMA operand fragment: 64 lanes x 16 B
 constexpr int kFragElems = 512;               // bf16 elements of one fragment
 constexpr int kStepElems = 4 * kFragElems;    // one 32-long step of one packed item
 constexpr int kXcds = 8;
-// tile height in 128-row wave rows: 2 (256 rows, 8 waves, one work-group
-// per CU) or 1 (128 rows, 4 waves, two work-groups per CU)
-constexpr int kWaveRows = 1;
-// ring slots: 4 x 32 KB (one work-group per CU) or 3 x 24 KB (two per CU)
-constexpr int kRingSlots = kWaveRows == 2 ? 4 : 3;
-
-// one 16-byte direct load per lane into the wave's 1 KB fragment at `frag`
-// in LDS (lane l's bytes land at frag + 16 l)
 using lds_void = __attribute__((address_space(3))) void;
-__device__ __forceinline__ void frag_load(const void* src, lds_void* frag) {
-  __builtin_amdgcn_global_load_lds(src, frag, 16, 0, 0);
-}
 
-// This wave's ring loads older than its last VM are in LDS and its LDS reads
-// have returned; then the work-group barrier.  The memory clobber keeps the
-// compiler from moving LDS reads across it.  (__syncthreads would also wait
-// for the loads still in flight for later steps.)
-template <int VM>
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
-}
+// Wave w owns items 2 w, 2 w + 1 of the tile.  A wave's weight fragments
+// are its own: they go from memory straight to registers, three steps ahead,
+// with no barrier.  Only the activation fragments are shared: an 8-slot LDS ring
+// filled by direct loads five steps ahead (each wave 2 of the 8 fragments of
+// a step), read one step ahead into a second register set, so that the reads
+// of step s + 1 overlap the MFMAs of step s.  A barrier every second step
+// orders the ring.  The memory counter drains in order: waiting for the
+// activations of steps s + 1, s + 2 (loaded at steps s - 4, s - 3) also
+// waits for the weights loaded before them, which are those of steps up to
+// s -- so the weights keep their three steps.
 
-// The 8 activation fragments and 4 weight fragments one wave uses in a
-// step: ds_read_b128 at a (+ 1 KB each) and b (+ 1 KB each), LDS byte
-// addresses, and the wait for all of them in the same statement.  Written
-// out because the compiler cannot tell which ring slot a direct load fills:
-// before its own LDS reads it would wait for every load in flight, also
-// those of later steps (ring_barrier orders the ring instead).
-// Early-clobber outputs: no result register may share a register with an
-// address.
-__device__ __forceinline__ void read_frags(uint32_t a, uint32_t b, u32x4_t (&av)[8],
-                                           u32x4_t (&bv)[4]) {
+constexpr int kWideItems = 8;        // packed items per wide tile (512 weight rows)
+constexpr int kASlotElems = 8 * 64;  // one activation slot: 8 fragments as u32x4 per lane
+constexpr int kWideSlots = 8;        // activation ring slots
+constexpr int kAAhead = 5;           // steps the activation loads run ahead
+constexpr int kBAhead = 3;           // steps the weight loads run ahead
+// epilogue staging: 16 rows of the 512-column tile, fp32, rows padded by 4
+// floats (the accumulator writes of a wave's four 4-row groups then fall in
+// different banks)
+constexpr int kStageLd = 512 + 4;
+
+// A direct load written out (16 B per lane to lds + 16 lane): the compiler
+// then does not see the ring being written and, before its own LDS reads,
+// waits for nothing (ring_barrier orders the ring); its waits for the weight
+// registers count one load fewer per ring load after them, i.e. wait for a
+// little more than needed.  M0 (the LDS address of the load) is saved and
+// restored around it.
+__device__ __forceinline__ void frag_load(const void* src, uint32_t lds) {
+  uint32_t m0_saved;
   asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %12 offset:1024\n\t"
-      "ds_read_b128 %2, %12 offset:2048\n\t"
-      "ds_read_b128 %3, %12 offset:3072\n\t"
-      "ds_read_b128 %4, %12 offset:4096\n\t"
-      "ds_read_b128 %5, %12 offset:5120\n\t"
-      "ds_read_b128 %6, %12 offset:6144\n\t"
-      "ds_read_b128 %7, %12 offset:7168\n\t"
-      "ds_read_b128 %8, %13\n\t"
-      "ds_read_b128 %9, %13 offset:1024\n\t"
-      "ds_read_b128 %10, %13 offset:2048\n\t"
-      "ds_read_b128 %11, %13 offset:3072\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3]), "=&v"(av[4]), "=&v"(av[5]),
-        "=&v"(av[6]), "=&v"(av[7]), "=&v"(bv[0]), "=&v"(bv[1]), "=&v"(bv[2]), "=&v"(bv[3])
-      : "v"(a), "v"(b)
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
       : "memory");
 }
 
-// LDS byte address of the ring
-template <int NB>
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t (&ring)[NB]) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (const __attribute__((address_space(3))) uint8_t*)&ring[0]));
+// This wave's loads older than its last VM are done (its ring loads are in
+// LDS); then the work-group barrier (other waves' loads of the same step
+// are in LDS too).
+template <int VM>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-template <bool GATEUP, int WR, int NS>
-__global__ __launch_bounds__(256 * WR, 2 / WR) void gemm_kernel(GroupedArgs a) {
-  // tile: 128 WR routed rows x 256 weight rows, 4 WR waves; per step the
-  // slot holds 8 WR activation fragments, then 16 weight fragments
-  constexpr int kAF = 8 * WR;                       // activation fragments per step
-  constexpr int kBW = 16 / (4 * WR);                // weight fragments each wave loads
-  constexpr int kLoads = 2 + kBW;                   // ring loads per wave per step
-  constexpr int kSlot = (kAF + 16) * kFragBytes;    // bytes of one slot
-  // NS slots of one 32-long step each: NS - 1 steps in flight
-  __shared__ __attribute__((aligned(kFragBytes))) uint8_t ring[NS * kSlot];
 
+// Two rows of 8 MFMAs (activation fragments a0, a1 against the 8 weight
+// fragments b) with two fragment reads of the next step (at lds + off0,
+// off1) issued in front of them and waited for at the end of the same
+// statement.  Written out so that the reads, and the loads the caller puts
+// between these statements, go out spread over the step's MFMAs: issued as
+// one burst after the barrier they hold up the MFMAs behind them.
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void mfma_rows2(f32x4_t (&c0)[8], f32x4_t (&c1)[8], const u32x4_t& a0,
+                                           const u32x4_t& a1, const u32x4_t (&b)[8], uint32_t lds,
+                                           u32x4_t& r0, u32x4_t& r1) {
+  asm volatile(
+      "ds_read_b128 %[r0], %[la] offset:%[o0]\n\t"
+      "ds_read_b128 %[r1], %[la] offset:%[o1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c04], %[a0], %[b4], %[c04]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c05], %[a0], %[b5], %[c05]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c06], %[a0], %[b6], %[c06]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c07], %[a0], %[b7], %[c07]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c14], %[a1], %[b4], %[c14]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c15], %[a1], %[b5], %[c15]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c16], %[a1], %[b6], %[c16]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c17], %[a1], %[b7], %[c17]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [c00] "+a"(c0[0]), [c01] "+a"(c0[1]), [c02] "+a"(c0[2]), [c03] "+a"(c0[3]),
+        [c04] "+a"(c0[4]), [c05] "+a"(c0[5]), [c06] "+a"(c0[6]), [c07] "+a"(c0[7]),
+        [c10] "+a"(c1[0]), [c11] "+a"(c1[1]), [c12] "+a"(c1[2]), [c13] "+a"(c1[3]),
+        [c14] "+a"(c1[4]), [c15] "+a"(c1[5]), [c16] "+a"(c1[6]), [c17] "+a"(c1[7]),
+        [r0] "=&v"(r0), [r1] "=&v"(r1)
+      : [a0] "v"(a0), [a1] "v"(a1), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
+        [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]), [b7] "v"(b[7]),
+        [la] "v"(lds), [o0] "i"(OFF0), [o1] "i"(OFF1)
+      : "memory");
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GroupedArgs a) {
+  __shared__ __attribute__((aligned(kFragBytes))) u32x4_t ring[kWideSlots * kASlotElems];
+  __shared__ __attribute__((aligned(16))) float stage[2 * 16 * kStageLd];
+  __shared__ int orows[128];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;
   const int H = a.H, I = a.I, k = a.k;
   const int K = GATEUP ? H : I;
-  // packed weights come in 128-long chunks, zero-padded: every step is computed
-  const int nsteps = ((K + 127) >> 7) * 4;
+  const int nsteps = ((K + 127) >> 7) * 4;  // a multiple of 4
   const int items = (GATEUP ? 2 * I : H) >> 6;
-  const int ntiles = (items + kTileItems - 1) / kTileItems;
+  const int ntiles = (items + kWideItems - 1) / kWideItems;
   const int32_t* groups = a.gemm_groups;
   const int n_units = groups[0] * ntiles;
   const int per_x = gridDim.x / kXcds;
@@ -139,17 +153,15 @@ __global__ __launch_bounds__(256 * WR, 2 / WR) void gemm_kernel(GroupedArgs a) {
     const int nt = unit - gi * ntiles;
     const int gv = groups[1 + gi];
     const int e = gv >> 16;
-    const int m0 = (gv & 0xffff) * (128 * WR);
+    const int m0 = (gv & 0xffff) * 128;
     const int off = a.offsets[e] + m0;
-    const int rows = min(128 * WR, a.offsets[e + 1] - off);
-    const int n_items = min(kTileItems, items - nt * kTileItems);
+    const int rows = min(128, a.offsets[e + 1] - off);
+    const int n_items = min(kWideItems, items - nt * kWideItems);
 
-    // This lane's part of the ring loads: activation fragments (row tiles)
-    // 2 wave and 2 wave + 1, weight fragments kBW wave .. + kBW - 1 (item
-    // f / 4 of the tile, 16-row tile f % 4).  Rows past the group's read its
-    // first row, items past the expert's its last item: loaded, never stored.
+    // activation fragments 2 wave, 2 wave + 1 of each step (rows past the
+    // group's read its first row); this wave's weight items (past the
+    // expert's: its last item, loaded and never used)
     const uint16_t* arow[2];
-    const uint16_t* bsrc[kBW];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int mt = 2 * wave + i;
@@ -157,116 +169,180 @@ __global__ __launch_bounds__(256 * WR, 2 / WR) void gemm_kernel(GroupedArgs a) {
       const int srow = GATEUP ? a.sorted_assign[off + m] / k : off + m;
       arow[i] = src + static_cast<size_t>(srow) * src_ld + 8 * g;
     }
+    const uint16_t* bsrc[2];
 #pragma unroll
-    for (int i = 0; i < kBW; ++i) {
-      const int f = kBW * wave + i;
-      const int item = min(nt * kTileItems + (f >> 2), items - 1);
-      bsrc[i] = wts + (static_cast<size_t>(e) * items + item) * nsteps * kStepElems +
-                (f & 3) * kFragElems + lane * 8;
+    for (int ii = 0; ii < 2; ++ii) {
+      const int item = min(nt * kWideItems + 2 * wave + ii, items - 1);
+      bsrc[ii] = wts + (static_cast<size_t>(e) * items + item) * nsteps * kStepElems + lane * 8;
     }
-    auto issue = [&](int s) {
-      const int at = (s % NS) * kSlot;
+    const bool busy = 2 * wave < n_items;
+    // the output row of routed row t of the group (down), for the epilogue
+    int orow_t = 0;
+    if (!GATEUP && t < rows) orow_t = a.tok_rows ? a.sorted_assign[off + t] : off + t;
+
+    // loads past the last step load the last step again (never read)
+    auto issue_a = [&](int s) {
+      u32x4_t* dst = ring + (s % kWideSlots) * kASlotElems;
       // activation elements past K: the last 8 of the row (their weights are 0)
-      const int kk = min(s * 32, K - 8 - 8 * g);
+      const int kk = min(min(s, nsteps - 1) * 32, K - 8 - 8 * g);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        frag_load(arow[i] + kk, (lds_void*)&ring[at + (2 * wave + i) * kFragBytes]);
-#pragma unroll
-      for (int i = 0; i < kBW; ++i)
-        frag_load(bsrc[i] + static_cast<size_t>(s) * kStepElems,
-                  (lds_void*)&ring[at + (kAF + kBW * wave + i) * kFragBytes]);
+        frag_load(arow[i] + kk, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                         (lds_void*)(dst + (2 * wave + i) * 64))));
     };
-
-    // this wave's row tiles that hold routed rows, and whether its item exists
-    const int mt_n = min(8, max(0, (rows - wm * 128 + 15) >> 4));
-    const bool busy = mt_n > 0 && wn < n_items;
-    f32x4_t acc[8][4];
+    u32x4_t bset[4][8];
+    auto load_b = [&](int s, u32x4_t(&bv)[8]) {
+      const size_t so = static_cast<size_t>(min(s, nsteps - 1)) * kStepElems;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        bv[q] = *reinterpret_cast<const u32x4_t*>(bsrc[q >> 2] + so + (q & 3) * kFragElems);
+    };
+    u32x4_t areg[2][8];
+    auto read_a = [&](int s, u32x4_t(&av)[8]) {
+      const u32x4_t* sl = ring + (s % kWideSlots) * kASlotElems;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) av[i] = sl[i * 64 + lane];
+    };
+    f32x4_t acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // this lane's byte offsets of its fragments within a slot
-    const uint32_t a_off = (wm * 8) * kFragBytes + lane * 16;
-    const uint32_t b_off = (kAF + wn * 4) * kFragBytes + lane * 16;
-    const uint32_t ring_base = lds_addr(ring);
-    auto compute = [&](int s) {
-      if (!busy) return;
-      u32x4_t av[8], bv[4];
-      const uint32_t base = ring_base + (s % NS) * kSlot;
-      read_frags(base + a_off, base + b_off, av, bv);
-      // only the row tiles that hold routed rows
+      for (int q = 0; q < 8; ++q) acc[i][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Step s (slot s mod 8, weight set s mod 4, activation registers s mod
+    // 2) computes with the fragments read during step s - 1 and reads those
+    // of step s + 1.  At the last step the reads are of a step that does not
+    // exist (the slot holds stale data, never used).
+    const uint32_t ring_lds =
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)ring)) + lane * 16;
+    auto load_b2 = [&](int s, u32x4_t(&bv)[8], int q0) {
+      const size_t so = static_cast<size_t>(min(s, nsteps - 1)) * kStepElems;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i >= mt_n) break;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
-                                                              __builtin_bit_cast(bf16x8_t, bv[q]),
-                                                              acc[i][q], 0, 0, 0);
-      }
+      for (int q = q0; q < q0 + 2; ++q)
+        bv[q] = *reinterpret_cast<const u32x4_t*>(bsrc[q >> 2] + so + (q & 3) * kFragElems);
     };
-    // Steps 0 .. NS-2 go out first; step s then waits for its own loads
-    // (kLoads per wave: the loads of the up to NS-2 steps issued after it
-    // stay in flight), and the barrier frees the slot of step s - 1 for step
-    // s + NS - 1.  nsteps >= 4 >= NS - 1.
-    constexpr int kAhead = NS - 1;
-    static_assert(kAhead <= 4, "at most four steps in flight");
+    // Every wave computes (one whose items are past the expert's works on
+    // the clamped weights; its results are not written).  The next step's
+    // fragment reads go out two per 16 MFMAs, the weight loads of step s + 3
+    // two between each 16.
+    auto step = [&](int s, auto rc) {
+      constexpr int R = decltype(rc)::value;
+      // Every second step: this wave's activation loads of steps s + 1 and
+      // s + 2 are done -- the later of them went out at step s - 3 after two
+      // weight loads, so the other 6 of that step and the 10 loads of each
+      // of steps s - 2, s - 1 may still be in flight -- and then the barrier:
+      // every wave is past step s - 1, so the slots of steps s - 3 and s - 2
+      // (read at steps s - 4 and s - 3) take the loads of steps s + 5, s + 6.
+      if ((R & 1) == 0) ring_barrier<6 + 2 * 10>();
+      const uint32_t la = ring_lds + ((s + 1) % kWideSlots) * (kASlotElems * 16);
+      u32x4_t(&an)[8] = areg[(R + 1) & 1];
+      const u32x4_t(&ac)[8] = areg[R & 1];
+      const u32x4_t(&bc)[8] = bset[R & 3];
+      u32x4_t(&bn)[8] = bset[(R + kBAhead) & 3];
+      mfma_rows2<0, 1024>(acc[0], acc[1], ac[0], ac[1], bc, la, an[0], an[1]);
+      load_b2(s + kBAhead, bn, 0);
+      issue_a(s + kAAhead);
+      mfma_rows2<2048, 3072>(acc[2], acc[3], ac[2], ac[3], bc, la, an[2], an[3]);
+      load_b2(s + kBAhead, bn, 2);
+      mfma_rows2<4096, 5120>(acc[4], acc[5], ac[4], ac[5], bc, la, an[4], an[5]);
+      load_b2(s + kBAhead, bn, 4);
+      mfma_rows2<6144, 7168>(acc[6], acc[7], ac[6], ac[7], bc, la, an[6], an[7]);
+      load_b2(s + kBAhead, bn, 6);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
 #pragma unroll
-    for (int p = 0; p < kAhead; ++p) issue(p);
-    for (int s = 0; s < nsteps; ++s) {
-      const int later = min(kAhead - 1, nsteps - 1 - s);  // steps issued after s
-      if (later >= 3)
-        ring_barrier<3 * kLoads>();
-      else if (later == 2)
-        ring_barrier<2 * kLoads>();
-      else if (later == 1)
-        ring_barrier<kLoads>();
-      else
-        ring_barrier<0>();
-      if (s + kAhead < nsteps) issue(s + kAhead);
-      compute(s);
+    for (int p = 0; p < kAAhead; ++p) issue_a(p);
+    asm volatile("" ::: "memory");  // the activation loads go out first
+#pragma unroll
+    for (int p = 0; p < kBAhead; ++p) load_b(p, bset[p]);
+    ring_barrier<8 * kBAhead>();  // the first steps' activations are in LDS
+    read_a(0, areg[0]);
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s, C0{});
+      step(s + 1, C1{});
+      step(s + 2, C2{});
+      step(s + 3, C3{});
     }
+    // the last MFMAs' results settle before the accumulators are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // epilogue: lane (r, g) holds D[m = 4g + jj][n = r] of each 16 x 16 tile
-    // (the ring is free for the next unit: its first loads go to the slots
-    // of the last unit's steps nsteps-4 .. nsteps-2, which every wave has
-    // finished with at the last barrier)
-    if (busy) {
+    // Epilogue, one 16-row slab of the tile at a time through LDS (two
+    // buffers): the waves write their accumulators (lane (r, g) holds
+    // D[4g + jj][r] of each 16 x 16 tile), then the work-group writes whole
+    // row segments with 16-byte stores -- down: the fp32 rows; gate/up: the
+    // SwiGLU of each 16-column tile's gate (columns 0..7) and up (8..15)
+    // halves, 8 bf16 of h per store.  Columns of items past the expert's
+    // are not written.
+    // (the thread index taken afresh: addresses derived from it are not
+    // hoisted out of the unit loop to stay live, in spilled registers,
+    // across the main loop)
+    int te = t;
+    asm volatile("" : "+v"(te));
+    const int re = te & 15, ge = (te >> 4) & 3, we = te >> 6;
+    if (!GATEUP && te < 128) orows[te] = orow_t;  // read after the first slab's barrier
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i >= mt_n) break;
-        int orow[4];
+    for (int i = 0; i < 8; ++i) {
+      if (i * 16 >= rows) break;
+      float* st = stage + (i & 1) * (16 * kStageLd);
+      if (busy) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int ml = (wm * 8 + i) * 16 + 4 * g + jj;
-          orow[jj] = -1;
-          if (ml < rows) orow[jj] = (!GATEUP && a.tok_rows) ? a.sorted_assign[off + ml] : off + ml;
-        }
+        for (int q = 0; q < 8; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int qq = (nt * kTileItems + wn) * 4 + q;  // 16-row tile of the expert
+          for (int jj = 0; jj < 4; ++jj)
+            st[(4 * ge + jj) * kStageLd + we * 128 + q * 16 + re] = acc[i][q][jj];
+      }
+      // the slab is in LDS (the stores of the last slab may still be in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (GATEUP) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float v = acc[i][q][jj];
-            if (GATEUP) {
-              // tile qq: gate rows 8 qq .. +7 in columns 0..7, up rows in 8..15
-              const float up = __shfl_xor(v, 8, kWave);
-              if (r < 8 && orow[jj] >= 0)
-                static_cast<uint16_t*>(a.h_perm)[static_cast<size_t>(orow[jj]) * I + 8 * qq + r] =
-                    f32_to_bf16(silu(v) * up);
-            } else if (orow[jj] >= 0) {
-              a.y_perm[static_cast<size_t>(orow[jj]) * H + qq * 16 + r] = v;
-            }
+        for (int it = 0; it < 2; ++it) {
+          const int u = it * 256 + te;
+          const int row = u >> 5, tile = u & 31;  // 16-column tile of the work-group's
+          const int ml = i * 16 + row;
+          if (ml >= rows || (tile >> 2) >= n_items) continue;
+          const float* gp = st + row * kStageLd + tile * 16;
+          const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
+          const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+          const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gp + 8);
+          const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gp + 12);
+          u32x4_t hv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float gl = c < 2 ? g0[2 * c] : g1[2 * c - 4];
+            const float gh = c < 2 ? g0[2 * c + 1] : g1[2 * c - 3];
+            const float ul = c < 2 ? u0[2 * c] : u1[2 * c - 4];
+            const float uh = c < 2 ? u0[2 * c + 1] : u1[2 * c - 3];
+            hv[c] = static_cast<uint32_t>(f32_to_bf16(silu(gl) * ul)) |
+                    (static_cast<uint32_t>(f32_to_bf16(silu(gh) * uh)) << 16);
           }
+          const int qq = nt * (kWideItems * 4) + tile;  // 16-row tile of the expert
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.h_perm) +
+                                      static_cast<size_t>(off + ml) * I + 8 * qq) = hv;
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int u = it * 256 + te;
+          const int row = u >> 7, col = (u & 127) * 4;
+          const int ml = i * 16 + row;
+          if (ml >= rows || col >= n_items * 64) continue;
+          const int orow = orows[ml];
+          *reinterpret_cast<f32x4_t*>(a.y_perm + static_cast<size_t>(orow) * H +
+                                      nt * (kWideItems * 64) + col) =
+              *reinterpret_cast<const f32x4_t*>(st + row * kStageLd + col);
         }
       }
     }
+    // every wave is done with the ring before the next unit's loads
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
 }  // namespace
 
-int gemm_tile_rows() { return 128 * kWaveRows; }
+int gemm_tile_rows() { return 128; }
 
 bool gemm_supported(const GroupedArgs& a) {
   return a.packed && a.w_kind == 1 && a.dense_n == 0 && a.w_slot == nullptr &&
@@ -274,9 +350,9 @@ bool gemm_supported(const GroupedArgs& a) {
 }
 
 hipError_t launch_gemm(const GroupedArgs& a, hipStream_t stream, int which) {
-  const int grid = (a.num_cu / kXcds) * kXcds * (2 / kWaveRows);
-  if (which != 2) gemm_kernel<true, kWaveRows, kRingSlots><<<grid, 256 * kWaveRows, 0, stream>>>(a);
-  if (which != 1) gemm_kernel<false, kWaveRows, kRingSlots><<<grid, 256 * kWaveRows, 0, stream>>>(a);
+  const int grid = (a.num_cu / kXcds) * kXcds;  // one work-group per CU
+  if (which != 2) gemm_kernel<true><<<grid, 256, 0, stream>>>(a);
+  if (which != 1) gemm_kernel<false><<<grid, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
