@@ -420,9 +420,8 @@ def main():
 def measured_traffic(workload):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary (FETCH_SIZE / WRITE_SIZE passes scaled by a known-size copy), or
-    None when there is none for this workload or the kernel source has
+    None when there is none for this workload or the kernel sources have
     changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -432,11 +431,23 @@ def measured_traffic(workload):
             rec = json.loads(line[len("traffic "):])
     if rec is None:
         return None
-    src = os.path.join(ROOT, "moe_speculative_decoding_gemm_amd", "csrc", "grouped.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("grouped_hip_sha256"):
+    if kernel_sources_sha256() != rec.get("kernel_sources_sha256"):
         return None
     return rec["bytes_per_launch"]
+
+
+# the sources the expert kernels are compiled from (grouped.hip and the
+# headers it includes)
+KERNEL_SOURCES = ("grouped.hip", "amoe_common.h", "amoe_launch.h")
+
+
+def kernel_sources_sha256():
+    """sha256 over the expert kernels' sources, in KERNEL_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "moe_speculative_decoding_gemm_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def moesd_sweep(args):
