@@ -330,6 +330,39 @@ def test_work_order_rounds_match_separate_path(lib, budget):
     assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
 
 
+def test_gemm_many_units_per_workgroup(lib):
+    """Every token routed to all 8 experts (k = E, natural routing): 4096 rows
+    per expert in 128-row groups, 3 column tiles per projection -- 768 GEMM
+    tiles per kernel, so each work-group runs several in sequence (the ring,
+    epilogue staging and output-row table reused across tiles).  y must be
+    the same bits as the streaming kernels' (the standalone grouped call)."""
+    cfg = W.CONFIGS["qwen3_30b"].with_(E=8, k=8, H=1536, I=768, N=4096, flags=1)
+    w = make_weights(cfg, device="cuda", gen_device="cpu")
+    b = W.make_block(cfg, 2)
+    say("gemm many units per work-group")
+    out, st = run_layer(lib, cfg, b, w, pack=True)
+    N, H, I, E, k = cfg.N, cfg.H, cfg.I, cfg.E, cfg.k
+    assert st["n_active"] == E
+    dev = "cuda"
+    e_ = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
+    ti, tg = out["topk_idx"], out["topk_gate"]
+    counts, offsets, sa, ip, act, na = e_(E), e_(E + 1), e_(N * k), e_(N * k), e_(E), e_(1)
+    lib.moe_route_permute(N, k, E, ti, counts, offsets, sa, ip, act, na)
+    w13, w2 = lib.pack_experts(shape_of(lib, cfg, w_layout=lib.LAYOUT_PACKED), w["w13"], w["w2"], E)
+    y_perm = e_(N * k, H, dt=torch.float32)
+    gws = torch.zeros(lib.moe_grouped_swiglu_workspace_size(N, k, I, 1), dtype=torch.uint8,
+                      device=dev)
+    d = upload_block(b)
+    lib.moe_grouped_swiglu(N, k, E, H, I, 1, 1, d["x"], w13, w2, None, None, offsets, sa, act,
+                           na, y_perm, gws, w_layout=lib.LAYOUT_PACKED)
+    y = e_(N, H, dt=torch.bfloat16)
+    lib.moe_combine(N, k, H, 1, y_perm, ip, tg, None, y)
+    torch.cuda.synchronize()
+    assert (counts.cpu().numpy() == N).all()
+    assert torch.equal(y.view(torch.int16), out["y"].view(torch.int16))
+    assert torch.isfinite(out["y"].float()).all()
+
+
 @pytest.mark.parametrize("over", [
     # natural routing, ~500 rows per expert: every expert in the GEMM tiles,
     # a partial last column tile (10 gate/up items), K = 320 padded to 384
