@@ -71,7 +71,7 @@ struct SelectArgs {
 // selection, restricted top-k, gates (and the grouping when counts is set)
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 void select_plan(int N, int H, int E, int num_cu, int* ksplit, int* kslice);
-int node_workgroups(int N);  // node groups of the front kernel
+int node_workgroups(int N, int E);  // node groups of the front kernel
 int group_chunks(int N, int k);  // chunks of the grouping for N > 256 (rows of ghist)
 size_t dpart_elems(int N, int E);  // doubles of d_part (expert-major rows of group partials)
 size_t fpart_bytes(int N, int E);  // bytes of f_part (same rows)

@@ -145,7 +145,7 @@ SelectWs carve_select(Carver& c, const acceptmoe_shape* s) {
   w.nat_idx = c.take<int32_t>(static_cast<size_t>(s->N) * s->k);
   w.nat_logit = c.take<float>(static_cast<size_t>(s->N) * s->k);
   w.ghist = c.take<int32_t>(static_cast<size_t>(amoe::group_chunks(s->N, s->k)) * s->E);
-  const size_t nwg = amoe::node_workgroups(s->N);
+  const size_t nwg = amoe::node_workgroups(s->N, s->E);
   w.d_part = c.take<double>(amoe::dpart_elems(s->N, s->E));
   w.f_part = c.take<uint8_t>(amoe::fpart_bytes(s->N, s->E));
   w.e_part = c.take<int32_t>(nwg);

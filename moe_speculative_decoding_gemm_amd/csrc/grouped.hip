@@ -41,6 +41,7 @@ namespace amoe {
 namespace {
 
 constexpr int kMT = 4;  // M tiles (16 rows each) per pass over the weights
+constexpr int kUnitTab = 64;  // work units whose parameters one table holds
 constexpr int kPackChunk = 128;  // reduction elements per packed chunk
 constexpr int kFragElems = 512;  // elements of one packed MFMA B fragment
 
@@ -472,33 +473,59 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
   // first item gets the lightest items of the later rounds
   const int C = a.num_cu;
   const bool snake = a.snake && !by_group && C > 0 && gridDim.x % C == 0;
-  for (int base = 0; base < n_units; base += gridDim.x) {
-    int unit = base + static_cast<int>(blockIdx.x);
-    if (snake && base == 0) {
-      const int q = unit / C, p = unit - q * C;
-      unit = q == 0 ? p : q * C + (C - 1 - p);
+  // The parameters of the work-group's next kUnitTab units, decoded by
+  // kUnitTab threads at once (group entry -> active expert -> offsets ->
+  // weight slot: a chain of dependent loads) into LDS, so that a unit starts
+  // its loads without that chain in front of them.
+  __shared__ int s_tab[8][kUnitTab];  // [0]: active index u (unused below)
+  const int n_iter = (n_units + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+  for (int i0 = 0; i0 < n_iter; i0 += kUnitTab) {
+    const int ni = min(kUnitTab, n_iter - i0);
+    __syncthreads();  // the last table's entries are read
+    if (t < ni) {
+      const int base = (i0 + t) * static_cast<int>(gridDim.x);
+      int unit = base + static_cast<int>(blockIdx.x);
+      if (snake && base == 0) {
+        const int q = unit / C, p = unit - q * C;
+        unit = q == 0 ? p : q * C + (C - 1 - p);
+      }
+      int u = 0, tile = 0, g0 = 0, rstep = 1, e = -1, off = 0, te = 0, ew = 0;
+      if (unit < n_units) {
+        if (by_group) {
+          const int gi = unit / tiles;
+          tile = unit - gi * tiles;
+          const int gv = a.groups[1 + gi];
+          u = gv >> 16;
+          g0 = gv & 0xffff;
+          rstep = 1 << 16;  // this group only
+        } else {
+          const int item = unit % n_items;
+          g0 = unit / n_items;
+          u = item / tiles;
+          tile = item - u * tiles;
+          rstep = R;
+        }
+        e = dense ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
+        off = dense ? u * a.N : a.offsets[e];
+        te = dense ? a.N : a.offsets[e + 1] - off;
+        // where expert e's weights sit
+        ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
+      }
+      s_tab[0][t] = u;
+      s_tab[1][t] = tile;
+      s_tab[2][t] = g0;
+      s_tab[3][t] = rstep;
+      s_tab[4][t] = e;
+      s_tab[5][t] = off;
+      s_tab[6][t] = te;
+      s_tab[7][t] = ew;
     }
-    if (unit >= n_units) continue;
-    int u, tile, g0, rstep;
-    if (by_group) {
-      const int gi = unit / tiles;
-      tile = unit - gi * tiles;
-      const int gv = a.groups[1 + gi];
-      u = gv >> 16;
-      g0 = gv & 0xffff;
-      rstep = 1 << 16;  // this group only
-    } else {
-      const int item = unit % n_items;
-      g0 = unit / n_items;
-      u = item / tiles;
-      tile = item - u * tiles;
-      rstep = R;
-    }
-    const int e = dense ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
-    const int off = dense ? u * a.N : a.offsets[e];
-    const int te = dense ? a.N : a.offsets[e + 1] - off;
-    // where expert e's weights sit
-    const int ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
+    __syncthreads();
+  for (int ii = 0; ii < ni; ++ii) {
+    const int e = s_tab[4][ii];
+    if (e < 0) continue;  // past the units
+    const int tile = s_tab[1][ii], g0 = s_tab[2][ii], rstep = s_tab[3][ii];
+    const int off = s_tab[5][ii], te = s_tab[6][ii], ew = s_tab[7][ii];
 
     const WTp* wrow[NT];
     int orow[NT];   // gate/up: intermediate index i; down: hidden index h
@@ -726,6 +753,7 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
         if constexpr (MTMAX >= 8) group(std::integral_constant<int, 8>{});
       }
     }
+  }
   }
 }
 

@@ -57,17 +57,20 @@ constexpr int kRankCountMax = 64;  // largest (padded) set whose restricted top-
 
 // nodes per group of the front kernel: 4 for blocks that the tail kernel
 // finishes (short latency chains), 16 above (a quarter of the router weight
-// re-reads and of the demand rows the tail sums)
-__host__ __device__ __forceinline__ int nodes_per_group(int N) {
-  return N > kFusedMaxN ? kNodesPerWGBig : kNodesPerWG;
+// re-reads and of the demand rows the tail sums) -- and above 64 nodes for
+// layers of more than 128 experts, whose demand rows dominate the tail
+// (DeepSeek-V3.1-shaped block, 256 nodes: tail 69 -> 48 us, front 60 -> 69
+// us; 128-expert layers of 128 and 256 nodes are faster with 4)
+__host__ __device__ __forceinline__ int nodes_per_group(int N, int E) {
+  return (N > kFusedMaxN || (N > 64 && E > 128)) ? kNodesPerWGBig : kNodesPerWG;
 }
 // demand / flag partial rows are stored expert-major, one row of group
 // partials per expert, padded so that a row starts 16-byte aligned
-__host__ __device__ __forceinline__ int node_groups(int N) {
-  return (N + nodes_per_group(N) - 1) / nodes_per_group(N);
+__host__ __device__ __forceinline__ int node_groups(int N, int E) {
+  return (N + nodes_per_group(N, E) - 1) / nodes_per_group(N, E);
 }
-__host__ __device__ __forceinline__ int dpart_stride(int N) { return (node_groups(N) + 1) & ~1; }
-__host__ __device__ __forceinline__ int fpart_stride(int N) { return (node_groups(N) + 15) & ~15; }
+__host__ __device__ __forceinline__ int dpart_stride(int N, int E) { return (node_groups(N, E) + 1) & ~1; }
+__host__ __device__ __forceinline__ int fpart_stride(int N, int E) { return (node_groups(N, E) + 15) & ~15; }
 
 // MFMA operand fragment: 8 consecutive K elements of one row (x or W_r).
 // v_mfma_f32_16x16x32_bf16: A[m][kk] in lane m + 16g for kk in [8g, 8g+8),
@@ -414,7 +417,7 @@ __device__ void select_set(const SelectArgs& a, int nwg, SetSmem& sm, CounterChe
   int f = 0;
   double dsum = 0.0;
   if (t < E) {
-    const int ds = dpart_stride(a.N), fs = fpart_stride(a.N);
+    const int ds = dpart_stride(a.N, a.E), fs = fpart_stride(a.N, a.E);
     const double* drow = a.d_part + static_cast<size_t>(t) * ds;
     const uint8_t* frow = a.f_part + static_cast<size_t>(t) * fs;
     constexpr int B = 8;  // 16-byte loads in flight per batch: 16 partials
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
                          whole_k && !logits_in ? sm.lg[slot] : nullptr);
   }
   __syncthreads();
-  const int ds = dpart_stride(N), fs = fpart_stride(N);
+  const int ds = dpart_stride(N, E), fs = fpart_stride(N, E);
   for (int x = t; x < E; x += 256) {
     double dsum = 0.0;
 #pragma unroll
@@ -920,7 +923,7 @@ __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) TailSmem sm;
   const int t = threadIdx.x;
   const int N = a.N, E = a.E;
-  const int nwg = node_groups(N);
+  const int nwg = node_groups(N, E);
   const bool fused = N <= kFusedMaxN;
   const CounterCheck cc = load_counters(a, nwg);
   if (!fused) {
@@ -1114,10 +1117,13 @@ __global__ __launch_bounds__(kTail) void group_scatter_kernel(SelectArgs a) {
 }  // namespace
 
 void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) {
-  // about 128 work-groups (groups x K slices), at most kMaxKSplit slices of
-  // at most kMaxSlice elements each, multiples of 64
-  const int groups = node_groups(N);
-  int ks = (128 + groups - 1) / groups;
+  // about 128 work-groups (groups x K slices) -- 256 for layers of more than
+  // 128 experts, whose router rows are long enough to fill the chip
+  // (DeepSeek-V3.1-shaped block: front 59 -> 52 us) -- at most kMaxKSplit
+  // slices of at most kMaxSlice elements each, multiples of 64
+  const int groups = node_groups(N, E);
+  const int target = E > 128 ? 256 : 128;
+  int ks = (target + groups - 1) / groups;
   if (ks > kMaxKSplit) ks = kMaxKSplit;
   const int min_ks = (H + kMaxSlice - 1) / kMaxSlice;
   if (ks < min_ks) ks = min_ks;
@@ -1126,13 +1132,12 @@ void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) 
   sl = (sl + 63) / 64 * 64;
   *kslice = sl;
   *ksplit = (H + sl - 1) / sl;
-  (void)E;
 }
 
-int node_workgroups(int N) { return node_groups(N); }
+int node_workgroups(int N, int E) { return node_groups(N, E); }
 int group_chunks(int N, int k) { return (N * k + kGroupChunk - 1) / kGroupChunk; }
-size_t dpart_elems(int N, int E) { return static_cast<size_t>(dpart_stride(N)) * E; }
-size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N)) * E; }
+size_t dpart_elems(int N, int E) { return static_cast<size_t>(dpart_stride(N, E)) * E; }
+size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N, E)) * E; }
 
 template <typename AT, int NPW>
 void launch_front(const SelectArgs& a, dim3 grid, int q, hipStream_t stream) {
@@ -1148,9 +1153,9 @@ void launch_front(const SelectArgs& a, dim3 grid, int q, hipStream_t stream) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const bool lin = (a.flags & kFlagLogitsIn) != 0;
-  const dim3 grid(node_groups(a.N), lin ? 1 : a.ksplit, 1);
+  const dim3 grid(node_groups(a.N, a.E), lin ? 1 : a.ksplit, 1);
   const int q = (a.E + kWave - 1) / kWave;
-  const bool big = nodes_per_group(a.N) == kNodesPerWGBig;
+  const bool big = nodes_per_group(a.N, a.E) == kNodesPerWGBig;
   if (a.act_bf16) {
     if (big)
       launch_front<uint16_t, kNodesPerWGBig>(a, grid, q, stream);
