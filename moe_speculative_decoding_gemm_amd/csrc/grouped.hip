@@ -426,7 +426,8 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const u32x2_t& u) {
 // quarter of the bytes per MFMA operation moved through the CU.  Each
 // output element is accumulated by the same MFMA sequence as in the default
 // tiling, so the results are the same bits.
-template <int WK, bool GATEUP, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false>
+template <int WK, bool GATEUP, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false,
+          bool DENSE = false>
 __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_kernel(GroupedArgs a) {
   static_assert(!PACKED || KC == kPackChunk, "packed weights come in 128-long chunks");
   static_assert(!PAIRED || (PACKED && NT == 2), "paired items: packed weights, two tiles a wave");
@@ -446,8 +447,9 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
   const int tiles = (GATEUP ? 2 * I : H) / (64 * NT);
   // dense mode: a.dense_n experts (a.active[0..dense_n), or expert u when
   // a.active is null) over every one of the N rows: expert u's rows are
-  // u*N .. u*N+N-1 of h_perm / y_perm, row m being node m's x
-  const bool dense = a.dense_n > 0;
+  // u*N .. u*N+N-1 of h_perm / y_perm, row m being node m's x (DENSE: the
+  // launcher picks it when a.dense_n > 0)
+  constexpr bool dense = DENSE;
   const int n_items = (dense ? a.dense_n : *a.n_active) * tiles;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 15, g = lane >> 4;
   const int nchunks = (K + KC - 1) / KC;
@@ -473,60 +475,41 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
   // first item gets the lightest items of the later rounds
   const int C = a.num_cu;
   const bool snake = a.snake && !by_group && C > 0 && gridDim.x % C == 0;
-  // The parameters of the work-group's next kUnitTab units, decoded by
-  // kUnitTab threads at once (group entry -> active expert -> offsets ->
-  // weight slot: a chain of dependent loads) into LDS, so that a unit starts
-  // its loads without that chain in front of them.
-  __shared__ int s_tab[8][kUnitTab];  // [0]: active index u (unused below)
-  const int n_iter = (n_units + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
-  for (int i0 = 0; i0 < n_iter; i0 += kUnitTab) {
-    const int ni = min(kUnitTab, n_iter - i0);
-    __syncthreads();  // the last table's entries are read
-    if (t < ni) {
-      const int base = (i0 + t) * static_cast<int>(gridDim.x);
-      int unit = base + static_cast<int>(blockIdx.x);
-      if (snake && base == 0) {
-        const int q = unit / C, p = unit - q * C;
-        unit = q == 0 ? p : q * C + (C - 1 - p);
-      }
-      int u = 0, tile = 0, g0 = 0, rstep = 1, e = -1, off = 0, te = 0, ew = 0;
-      if (unit < n_units) {
-        if (by_group) {
-          const int gi = unit / tiles;
-          tile = unit - gi * tiles;
-          const int gv = a.groups[1 + gi];
-          u = gv >> 16;
-          g0 = gv & 0xffff;
-          rstep = 1 << 16;  // this group only
-        } else {
-          const int item = unit % n_items;
-          g0 = unit / n_items;
-          u = item / tiles;
-          tile = item - u * tiles;
-          rstep = R;
-        }
-        e = dense ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
-        off = dense ? u * a.N : a.offsets[e];
-        te = dense ? a.N : a.offsets[e + 1] - off;
-        // where expert e's weights sit
-        ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
-      }
-      s_tab[0][t] = u;
-      s_tab[1][t] = tile;
-      s_tab[2][t] = g0;
-      s_tab[3][t] = rstep;
-      s_tab[4][t] = e;
-      s_tab[5][t] = off;
-      s_tab[6][t] = te;
-      s_tab[7][t] = ew;
+  // A unit's parameters: group entry -> active expert -> offsets -> weight
+  // slot, a chain of dependent loads.
+  auto decode = [&](int unit, bool first, int& tile, int& g0, int& rstep, int& e, int& off,
+                    int& te, int& ew) {
+    if (snake && first) {  // unit == blockIdx.x
+      const int q = unit / C, p = unit - q * C;
+      unit = q == 0 ? p : q * C + (C - 1 - p);
     }
-    __syncthreads();
-  for (int ii = 0; ii < ni; ++ii) {
-    const int e = s_tab[4][ii];
-    if (e < 0) continue;  // past the units
-    const int tile = s_tab[1][ii], g0 = s_tab[2][ii], rstep = s_tab[3][ii];
-    const int off = s_tab[5][ii], te = s_tab[6][ii], ew = s_tab[7][ii];
-
+    tile = 0, g0 = 0, rstep = 1, e = -1, off = 0, te = 0, ew = 0;
+    if (unit < n_units) {
+      int u;
+      if (by_group) {
+        const int gi = unit / tiles;
+        tile = unit - gi * tiles;
+        const int gv = a.groups[1 + gi];
+        u = gv >> 16;
+        g0 = gv & 0xffff;
+        rstep = 1 << 16;  // this group only
+      } else {
+        const int item = unit % n_items;
+        g0 = unit / n_items;
+        u = item / tiles;
+        tile = item - u * tiles;
+        rstep = R;
+      }
+      e = DENSE ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
+      off = DENSE ? u * a.N : a.offsets[e];
+      te = DENSE ? a.N : a.offsets[e + 1] - off;
+      // where expert e's weights sit
+      ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
+    }
+  };
+  // One unit: the item's weights against its routed-row groups.
+  auto run_unit = [&](const int e, const int tile, const int g0, const int rstep, const int off,
+                      const int te, const int ew) {
     const WTp* wrow[NT];
     int orow[NT];   // gate/up: intermediate index i; down: hidden index h
     int srow[NT];   // row of the weight matrix selected by the scale grid
@@ -574,14 +557,17 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
         // read row 0 of the group instead (their results are never stored), so
         // every load below is unconditional: guarded loads would make the
         // compiler's wait counting fall back to waiting for all of them.
-        const uint16_t* src[PV];
+        // (as 32-bit element offsets from src_base -- at most N*k rows of at
+        // most 16384 elements, below 2^31 -- one register each, the base in
+        // scalar registers)
+        uint32_t src[PV];
         const int kk = (t % TPR) * 8;
 #pragma unroll
         for (int p = 0; p < PV; ++p) {
           const int rr = p * RPP + t / TPR;
           const int m = mg + rr < te ? mg + rr : mg;
           const int srcrow = GATEUP ? (dense ? m : a.sorted_assign[off + m] / k) : off + m;
-          src[p] = src_base + static_cast<size_t>(srcrow) * src_ld;
+          src[p] = static_cast<uint32_t>(srcrow) * static_cast<uint32_t>(src_ld);
         }
         f32x4_t acc[NT][MTV];
 #pragma unroll
@@ -603,7 +589,7 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
         auto stage_load = [&](u32x4_t (&v)[PV], int c) {
           const int k0 = min(c * KC + kk, K - 8);
 #pragma unroll
-          for (int p = 0; p < PV; ++p) v[p] = *reinterpret_cast<const u32x4_t*>(src[p] + k0);
+          for (int p = 0; p < PV; ++p) v[p] = *reinterpret_cast<const u32x4_t*>(src_base + (src[p] + k0));
         };
         auto stage_store = [&](const u32x4_t (&v)[PV], int buf) {
 #pragma unroll
@@ -691,7 +677,7 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
         // behind the pipeline's loads and used only by the epilogue
         const bool tok = !GATEUP && a.tok_rows && !dense;
         int my_row = 0;
-        if (tok && t < ROWS) my_row = a.sorted_assign[off + min(mg + t, te - 1)];
+        if (tok) my_row = a.sorted_assign[off + min(mg + (ROWS <= kWave ? lane : t), te - 1)];
         stage_store(sv[0], 0);
         __syncthreads();
         // chunk c: weights in ring slot c % DW, activations in VGPR ring / LDS
@@ -753,7 +739,71 @@ __global__ __launch_bounds__(256, (WK == 2 && !PAIRED) ? 2 : 1) void expert_lds_
         if constexpr (MTMAX >= 8) group(std::integral_constant<int, 8>{});
       }
     }
+  };
+  // A work-group with more than one unit has the parameters of its next
+  // kUnitTab units decoded by kUnitTab threads at once into LDS, so that a
+  // unit starts its loads without the chain in front of them; with one unit
+  // every thread decodes it itself (no barriers).
+  // (bf16 only: a second copy of the unit code raises the FP8 kernels'
+  // register pressure past their budget of two work-groups per CU)
+  const int n_iter = (n_units + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+  if constexpr (WK == 1) {
+    if (n_iter <= 1) {
+      int tile, g0, rstep, e, off, te, ew;
+      decode(static_cast<int>(blockIdx.x), true, tile, g0, rstep, e, off, te, ew);
+      if (e >= 0) run_unit(e, tile, g0, rstep, off, te, ew);
+      return;
+    }
   }
+  __shared__ int s_tab[7][kUnitTab];
+  for (int i0 = 0; i0 < n_iter; i0 += kUnitTab) {
+    const int ni = min(kUnitTab, n_iter - i0);
+    __syncthreads();  // the last table's entries are read
+    if (t < ni) {
+      const int base = (i0 + t) * static_cast<int>(gridDim.x);
+      int unit = base + static_cast<int>(blockIdx.x);
+      if (snake && base == 0) {
+        const int q = unit / C, p = unit - q * C;
+        unit = q == 0 ? p : q * C + (C - 1 - p);
+      }
+      int tile = 0, g0 = 0, rstep = 1, e = -1, off = 0, te = 0, ew = 0;
+      if (unit < n_units) {
+        int u;
+        if (by_group) {
+          const int gi = unit / tiles;
+          tile = unit - gi * tiles;
+          const int gv = a.groups[1 + gi];
+          u = gv >> 16;
+          g0 = gv & 0xffff;
+          rstep = 1 << 16;  // this group only
+        } else {
+          const int item = unit % n_items;
+          g0 = unit / n_items;
+          u = item / tiles;
+          tile = item - u * tiles;
+          rstep = R;
+        }
+        e = DENSE ? (a.active ? min(max(a.active[u], 0), a.E - 1) : u) : a.active[u];
+        off = DENSE ? u * a.N : a.offsets[e];
+        te = DENSE ? a.N : a.offsets[e + 1] - off;
+        ew = a.w_slot ? min(max(a.w_slot[e], 0), a.n_wslots - 1) : e;
+      }
+      s_tab[0][t] = tile;
+      s_tab[1][t] = g0;
+      s_tab[2][t] = rstep;
+      s_tab[3][t] = e;
+      s_tab[4][t] = off;
+      s_tab[5][t] = te;
+      s_tab[6][t] = ew;
+    }
+    __syncthreads();
+    for (int ii = 0; ii < ni; ++ii) {
+      // the same for every lane: scalar registers
+      const auto rd = [&](int f) { return __builtin_amdgcn_readfirstlane(s_tab[f][ii]); };
+      const int e = rd(3);
+      if (e < 0) continue;  // past the units
+      run_unit(e, rd(0), rd(1), rd(2), rd(4), rd(5), rd(6));
+    }
   }
 }
 
@@ -841,27 +891,29 @@ int resident_per_cu(Kern kern, int fallback) {
   return n;
 }
 
-template <int WK, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false>
+template <int WK, int NT, int KC, bool PACKED, int MTMAX = 4, bool PAIRED = false,
+          bool DENSE = false>
 void launch_lds(const GroupedArgs& a, hipStream_t stream, int which) {
   static const int occ_g =
-      resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED>, 2);
+      resident_per_cu(expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED, DENSE>, 2);
   static const int occ_d =
-      resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED>, 2);
+      resident_per_cu(expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED, DENSE>, 2);
   const int max_active = a.dense_n > 0 ? a.dense_n : (a.E < a.N * a.k ? a.E : a.N * a.k);
   const int R = a.row_groups > 1 ? a.row_groups : 1;
   if (which != 2) {
     const int items = max_active * (2 * a.I / (64 * NT)) * R;
     const int grid = items < occ_g * a.num_cu ? items : occ_g * a.num_cu;
-    expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED><<<grid, 256, 0, stream>>>(a);
+    expert_lds_kernel<WK, true, NT, KC, PACKED, MTMAX, PAIRED, DENSE><<<grid, 256, 0, stream>>>(a);
   }
   if (which != 1) {
     const int items = max_active * (a.H / (64 * NT)) * R;
     const int grid = items < occ_d * a.num_cu ? items : occ_d * a.num_cu;
-    expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED><<<grid, 256, 0, stream>>>(a);
+    expert_lds_kernel<WK, false, NT, KC, PACKED, MTMAX, PAIRED, DENSE><<<grid, 256, 0, stream>>>(a);
   }
 }
 
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which) {
+  const bool dense = a.dense_n > 0;
   switch (a.w_kind) {
     case 0:
       launch_wk<0>(a, stream, which);
@@ -869,16 +921,24 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream, int which) {
     case 1:
       if (a.packed && a.gemm)
         launch_lds<1, 2, kPackChunk, true, 8, true>(a, stream, which);
+      else if (a.packed && dense)
+        launch_lds<1, kPackNT_bf16, kPackChunk, true, 4, false, true>(a, stream, which);
       else if (a.packed)
         launch_lds<1, kPackNT_bf16, kPackChunk, true>(a, stream, which);
+      else if (dense)
+        launch_lds<1, 1, 128, false, 4, false, true>(a, stream, which);
       else
         launch_lds<1, 1, 128, false>(a, stream, which);
       break;
     default:
       if (a.packed && a.gemm)
         launch_lds<2, 2, kPackChunk, true, 8, true>(a, stream, which);
+      else if (a.packed && dense)
+        launch_lds<2, kPackNT_fp8, kPackChunk, true, 4, false, true>(a, stream, which);
       else if (a.packed)
         launch_lds<2, kPackNT_fp8, kPackChunk, true>(a, stream, which);
+      else if (dense)
+        launch_lds<2, 1, 128, false, 4, false, true>(a, stream, which);
       else
         launch_lds<2, 1, 128, false>(a, stream, which);
       break;
