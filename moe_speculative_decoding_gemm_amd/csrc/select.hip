@@ -66,6 +66,11 @@ __host__ __device__ __forceinline__ int nodes_per_group(int N, int E) {
 }
 // demand / flag partial rows are stored expert-major, one row of group
 // partials per expert, padded so that a row starts 16-byte aligned
+// waves of a front work-group: one per node of a 4-node group; 8 for a
+// 16-node group (2 nodes each in the node phase, 1 or 2 expert tiles each in
+// the router product)
+template <int NPW>
+constexpr int front_waves() { return NPW > kNodesPerWG ? 8 : 4; }
 __host__ __device__ __forceinline__ int node_groups(int N, int E) {
   return (N + nodes_per_group(N, E) - 1) / nodes_per_group(N, E);
 }
@@ -572,6 +577,8 @@ __device__ __forceinline__ void active_stats(int NK, int E, const int32_t* sel,
 // top-k and softmax statistics: every node's top-k over the eligible set, the
 // gates, and (when a.counts is set) the grouping of the assignments by expert.
 // lg_lds: sm.lg holds the logits (else they are read from a.logits).
+// SPLIT: the grouping's split mode (a.split_rows >= 0) is on
+template <bool SPLIT>
 __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) {
   const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
   const int N = a.N, E = a.E, k = a.k;
@@ -744,7 +751,7 @@ __device__ void restricted_tail(const SelectArgs& a, TailSmem& sm, bool lg_lds) 
     permute_block<kTail>(N, k, E, sm.top_e, a.counts, a.offsets, a.sorted_assign, a.inv_pos,
                        a.active, a.n_active, a.resident, static_cast<StatsDev*>(a.stats),
                        sm.u.perm, a.max_rows, a.groups, a.active_w, a.group_shift,
-                       a.split_rows, a.n_work);
+                       SPLIT ? a.split_rows : -1, SPLIT ? a.n_work : nullptr);
   else
     active_stats<kTail>(NK, E, sm.top_e, a.resident, static_cast<StatsDev*>(a.stats),
                         sm.set.rank);
@@ -788,7 +795,7 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
   const AT* wrow[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int e = min((wave + 4 * tt) * 16 + mrow, E - 1);
+    const int e = min((wave + front_waves<NPW>() * tt) * 16 + mrow, E - 1);
     wrow[tt] = static_cast<const AT*>(a.w_router) + static_cast<size_t>(e) * H + kbeg + kq;
   }
   f32x4_t acc[TPW];
@@ -821,7 +828,7 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
   if (NPW > kNodesPerWG || gq == 0) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      const int e = (wave + 4 * tt) * 16 + (lane & 15);
+      const int e = (wave + front_waves<NPW>() * tt) * 16 + (lane & 15);
       if (e < E) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -837,11 +844,13 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
 }
 
 // ------------------------------------------------------------- kernel ----
-// Q: 64-expert slots per lane, ceil(E / 64); NPW nodes per group (wave w
-// takes nodes n0 + w, n0 + w + 4, ... in the node phase)
+// Q: 64-expert slots per lane, ceil(E / 64); NPW nodes per group (wave w of
+// NW takes nodes n0 + w, n0 + w + NW, ... in the node phase)
 template <typename AT, int Q, int NPW>
-__global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
-  constexpr int PER_WAVE = NPW / 4;
+__global__ __launch_bounds__(64 * front_waves<NPW>()) void front_kernel(SelectArgs a) {
+  constexpr int NW = front_waves<NPW>();
+  constexpr int NTHR = 64 * NW;
+  constexpr int PER_WAVE = NPW / NW;
   __shared__ NodeSmem<NPW> sm;
   const int t = threadIdx.x, wave = t >> 6, lane = lane_id();
   const int g = blockIdx.x, ks = blockIdx.y;
@@ -859,7 +868,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   float cf[PER_WAVE];
 #pragma unroll
   for (int s = 0; s < PER_WAVE; ++s) {
-    const int nd = min(n0 + wave + 4 * s, N - 1);
+    const int nd = min(n0 + wave + NW * s, N - 1);
     d[s] = a.depth[nd];
     p[s] = a.parent[nd];
   }
@@ -870,7 +879,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   }
   if (!logits_in) {
     // ---- partial logits of the group's nodes over K slice ks
-    const int tpw = ((E + 15) / 16 + 3) / 4;  // 16-expert tiles per wave
+    const int tpw = ((E + 15) / 16 + NW - 1) / NW;  // 16-expert tiles per wave
     float (*lds)[kMaxE] = whole_k ? sm.lg : nullptr;
     const int node = n0 + wave;
     if (tpw == 1)
@@ -886,11 +895,11 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   }
   if (logits_in || NPW > kNodesPerWG) {
 #pragma unroll
-    for (int s = 0; s < PER_WAVE; ++s) node_deps(a, n0 + wave + 4 * s, d[s], p[s], cf[s], dp[s]);
+    for (int s = 0; s < PER_WAVE; ++s) node_deps(a, n0 + wave + NW * s, d[s], p[s], cf[s], dp[s]);
   }
 
   // ---- node phase (the group's last K-slice work-group)
-  for (int x = t; x < kMaxE; x += 256) {
+  for (int x = t; x < kMaxE; x += NTHR) {
     sm.flags[x] = 0;
 #pragma unroll
     for (int w = 0; w < NPW; ++w) sm.c[w][x] = 0.0;
@@ -899,14 +908,14 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < PER_WAVE; ++s) {
-    const int slot = wave + 4 * s;
+    const int slot = wave + NW * s;
     if (n0 + slot < N)
       node_phase<Q, NPW>(a, n0 + slot, slot, sm, d[s], p[s], dp[s], cf[s], bias,
                          whole_k && !logits_in ? sm.lg[slot] : nullptr);
   }
   __syncthreads();
   const int ds = dpart_stride(N, E), fs = fpart_stride(N, E);
-  for (int x = t; x < E; x += 256) {
+  for (int x = t; x < E; x += NTHR) {
     double dsum = 0.0;
 #pragma unroll
     for (int w = 0; w < NPW; ++w) dsum += sm.c[w][x];  // node order
@@ -919,6 +928,7 @@ __global__ __launch_bounds__(256) void front_kernel(SelectArgs a) {
 // The set selection and, for N <= kFusedMaxN, every node's restricted top-k,
 // the gates and the grouping: one work-group of kTail threads, after the
 // front kernel.  The node phase's outputs are loaded first, all together.
+template <bool SPLIT>
 __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) TailSmem sm;
   const int t = threadIdx.x;
@@ -976,7 +986,7 @@ __global__ __launch_bounds__(kTail) void tail_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  restricted_tail(a, sm, lg_lds);
+  restricted_tail<SPLIT>(a, sm, lg_lds);
 }
 
 // one wave per node, 4 nodes per work-group (N > kFusedMaxN)
@@ -1141,14 +1151,15 @@ size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N, E)
 
 template <typename AT, int NPW>
 void launch_front(const SelectArgs& a, dim3 grid, int q, hipStream_t stream) {
+  const int nthr = 64 * front_waves<NPW>();
   if (q == 1)
-    front_kernel<AT, 1, NPW><<<grid, 256, 0, stream>>>(a);
+    front_kernel<AT, 1, NPW><<<grid, nthr, 0, stream>>>(a);
   else if (q == 2)
-    front_kernel<AT, 2, NPW><<<grid, 256, 0, stream>>>(a);
+    front_kernel<AT, 2, NPW><<<grid, nthr, 0, stream>>>(a);
   else if (q == 3)
-    front_kernel<AT, 3, NPW><<<grid, 256, 0, stream>>>(a);
+    front_kernel<AT, 3, NPW><<<grid, nthr, 0, stream>>>(a);
   else
-    front_kernel<AT, 4, NPW><<<grid, 256, 0, stream>>>(a);
+    front_kernel<AT, 4, NPW><<<grid, nthr, 0, stream>>>(a);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
@@ -1167,7 +1178,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     else
       launch_front<float, kNodesPerWG>(a, grid, q, stream);
   }
-  tail_kernel<<<1, kTail, 0, stream>>>(a);
+  if (a.split_rows >= 0)
+    tail_kernel<true><<<1, kTail, 0, stream>>>(a);
+  else
+    tail_kernel<false><<<1, kTail, 0, stream>>>(a);
   if (a.N > kFusedMaxN) {
     restricted_kernel<<<(a.N + kNodesPerWG - 1) / kNodesPerWG, 256, 0, stream>>>(a);
     if (a.counts) {
