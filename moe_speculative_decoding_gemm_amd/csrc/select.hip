@@ -55,14 +55,15 @@ constexpr int kLgCap = 8192;     // logits the tail holds in LDS (N * E up to th
 constexpr int kTail = 1024;      // threads of the tail kernel (one work-group)
 constexpr int kRankCountMax = 64;  // largest (padded) set whose restricted top-k counts ranks
 
-// nodes per group of the front kernel: 4 for blocks that the tail kernel
-// finishes (short latency chains), 16 above (a quarter of the router weight
-// re-reads and of the demand rows the tail sums) -- and above 64 nodes for
-// layers of more than 128 experts, whose demand rows dominate the tail
-// (DeepSeek-V3.1-shaped block, 256 nodes: tail 69 -> 48 us, front 60 -> 69
-// us; 128-expert layers of 128 and 256 nodes are faster with 4)
+// nodes per group of the front kernel: 4 for blocks up to 128 nodes (64 for
+// layers of more than 128 experts), 16 above (a quarter of the router weight
+// re-reads and of the demand rows the tail sums; 8 waves, two nodes each in
+// the node phase).  Measured: DeepSeek-V3.1-shaped block (256 nodes, 256
+// experts) front + tail 111 -> 90 us; 128-expert layers at 256 nodes 216.5 ->
+// 213.3 us, at 128 nodes equal, at 64 nodes 4-node groups are faster
+// (135.7 -> 141.8 us).
 __host__ __device__ __forceinline__ int nodes_per_group(int N, int E) {
-  return (N > kFusedMaxN || (N > 64 && E > 128)) ? kNodesPerWGBig : kNodesPerWG;
+  return (N > 128 || (N > 64 && E > 128)) ? kNodesPerWGBig : kNodesPerWG;
 }
 // demand / flag partial rows are stored expert-major, one row of group
 // partials per expert, padded so that a row starts 16-byte aligned
@@ -1129,10 +1130,12 @@ __global__ __launch_bounds__(kTail) void group_scatter_kernel(SelectArgs a) {
 void select_plan(int N, int H, int E, int /*num_cu*/, int* ksplit, int* kslice) {
   // about 128 work-groups (groups x K slices) -- 256 for layers of more than
   // 128 experts, whose router rows are long enough to fill the chip
-  // (DeepSeek-V3.1-shaped block: front 59 -> 52 us) -- at most kMaxKSplit
-  // slices of at most kMaxSlice elements each, multiples of 64
+  // (DeepSeek-V3.1-shaped block: front 59 -> 52 us), and above 512 nodes
+  // (128-expert layer at 1024 nodes: 348 -> 341 us; at 256 and 512 nodes
+  // 128 are as fast or faster) -- at most kMaxKSplit slices of at most
+  // kMaxSlice elements each, multiples of 64
   const int groups = node_groups(N, E);
-  const int target = E > 128 ? 256 : 128;
+  const int target = (E > 128 || N > 512) ? 256 : 128;
   int ks = (target + groups - 1) / groups;
   if (ks > kMaxKSplit) ks = kMaxKSplit;
   const int min_ks = (H + kMaxSlice - 1) / kMaxSlice;
