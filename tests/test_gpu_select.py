@@ -48,6 +48,12 @@ SMALL = [
     ("qwen3_235b_b4", dict(E=64, k=8, H=192, N=64)),
     ("dsv31", dict(E=200, k=8, H=384, N=96, n_chains=12, chain_len=8)),
     ("qwen3_30b", dict(E=256, k=16, H=128, N=300)),
+    # 16-node router groups in 8-wave work-groups, fused tail: a ragged last
+    # group (203 = 12 x 16 + 11), 7 expert tiles over 8 waves
+    ("qwen3_30b", dict(E=100, k=6, H=320, N=203)),
+    # the same for more than 128 experts from 65 nodes: 10 tiles (two waves
+    # take two), last group of 8
+    ("dsv31", dict(E=160, k=8, H=256, N=72, n_chains=9, chain_len=8)),
 ]
 
 
