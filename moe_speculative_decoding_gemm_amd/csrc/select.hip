@@ -39,6 +39,8 @@
 
 #include "amoe_common.h"
 #include "amoe_launch.h"
+
+#include <type_traits>
 #include "amoe_permute.h"
 
 namespace amoe {
@@ -802,6 +804,50 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
   f32x4_t acc[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (NPW > kNodesPerWG && nsteps > S) {
+    // 16-node groups (8 waves, long K slices): two batches of S steps in
+    // flight, the loads of batch b + 1 issued before batch b's MFMAs.  Loads
+    // past the slice inside a batch read its last step again (never used),
+    // so the memory counter waits only for the batch it needs.
+    RFrag<AT> bf[2][TPW][S];
+    RFrag<AT> af[2][S];
+    auto load_batch = [&](auto bc, int s0) {
+      constexpr int b = decltype(bc)::value;
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int s = 0; s < S; ++s) bf[b][tt][s].load(wrow[tt] + 32 * min(s0 + s, nsteps - 1));
+#pragma unroll
+      for (int s = 0; s < S; ++s) af[b][s].load(xrow + 32 * min(s0 + s, nsteps - 1));
+    };
+    auto compute_batch = [&](auto bc, int s0) {
+      constexpr int b = decltype(bc)::value;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (s0 + s < nsteps) {
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) acc[tt] = rmma(af[b][s], bf[b][tt][s], acc[tt]);
+        }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    load_batch(B0{}, 0);
+    int s0 = 0;
+    for (; s0 + 2 * S < nsteps; s0 += 2 * S) {
+      load_batch(B1{}, s0 + S);
+      compute_batch(B0{}, s0);
+      load_batch(B0{}, s0 + 2 * S);
+      compute_batch(B1{}, s0 + S);
+    }
+    // the last one or two batches, without loads past them
+    if (s0 + S < nsteps) {
+      load_batch(B1{}, s0 + S);
+      compute_batch(B0{}, s0);
+      compute_batch(B1{}, s0 + S);
+    } else {
+      compute_batch(B0{}, s0);
+    }
+  } else
   for (int s0 = 0; s0 < nsteps; s0 += S) {
     RFrag<AT> bf[TPW][S];
     RFrag<AT> af[S];
@@ -883,14 +929,18 @@ __global__ __launch_bounds__(64 * front_waves<NPW>()) void front_kernel(SelectAr
     const int tpw = ((E + 15) / 16 + NW - 1) / NW;  // 16-expert tiles per wave
     float (*lds)[kMaxE] = whole_k ? sm.lg : nullptr;
     const int node = n0 + wave;
+    // (8 waves: at most 2 tiles each for kMaxE experts)
+    static_assert(kMaxE <= 16 * 2 * 8, "8-wave router groups take at most 2 tiles a wave");
     if (tpw == 1)
       router_partials<AT, 1, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
-    else if (tpw == 2)
+    else if (NW == 8 || tpw == 2)
       router_partials<AT, 2, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
-    else if (tpw == 3)
-      router_partials<AT, 3, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
-    else
-      router_partials<AT, 4, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
+    else if constexpr (NW == 4) {
+      if (tpw == 3)
+        router_partials<AT, 3, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
+      else
+        router_partials<AT, 4, NPW>(a, g, ks, wave, lane, node, d[0], p[0], cf[0], dp[0], lds);
+    }
     // partials travel at device scope: no cache write-back or invalidation
     if (!whole_k && !last_arrival_dev(&a.gcount[g], gridDim.y, &a.counters[0])) return;
   }
