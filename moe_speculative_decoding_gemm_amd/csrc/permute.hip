@@ -41,31 +41,34 @@ __global__ void shared_grouping_kernel(int N, int32_t* offsets, int32_t* sorted_
 // summed in slot order j = 0..k-1; all loads of a thread are issued up front.
 // kTok: the rows are already in token-major order (row i*k + j), so the
 // loads need no inv_pos round trip first; the arithmetic is the same.
-template <bool kBf16, bool kTok>
+// KK > 0: k is KK (the loops have no bounds to test at run time); 0: k as
+// given.
+template <bool kBf16, bool kTok, int KK>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
-  const int N = c.N, k = c.k, H = c.H;
+  const int N = c.N, k = KK > 0 ? KK : c.k, H = c.H;
+  constexpr int KM = KK > 0 ? KK : kMaxK;
   const int h4 = H >> 2;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<size_t>(N) * h4) return;
   const int i = static_cast<int>(idx / h4);
   const int h = static_cast<int>(idx - static_cast<size_t>(i) * h4) * 4;
-  const float* src[kMaxK];
-  float g[kMaxK];
+  const float* src[KM];
+  float g[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j < k) {
       const int row = kTok ? i * k + j : c.inv_pos[static_cast<size_t>(i) * k + j];
       src[j] = c.y_perm + static_cast<size_t>(row) * H;
       g[j] = c.gate[static_cast<size_t>(i) * k + j];
     }
   }
-  f32x4_t v[kMaxK];
+  f32x4_t v[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
+  for (int j = 0; j < KM; ++j)
     if (j < k) v[j] = *reinterpret_cast<const f32x4_t*>(src[j] + h);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
+  for (int j = 0; j < KM; ++j)
     if (j < k) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(g[j], v[j][q], acc[q]);
@@ -82,12 +85,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
   }
 }
 
+template <bool kBf16, int KK>
+void launch_combine_k(const CombineArgs& c, unsigned blocks, hipStream_t stream) {
+  if (c.inv_pos)
+    combine_kernel<kBf16, false, KK><<<blocks, 256, 0, stream>>>(c);
+  else
+    combine_kernel<kBf16, true, KK><<<blocks, 256, 0, stream>>>(c);
+}
 template <bool kBf16>
 void launch_combine_t(const CombineArgs& c, unsigned blocks, hipStream_t stream) {
-  if (c.inv_pos)
-    combine_kernel<kBf16, false><<<blocks, 256, 0, stream>>>(c);
+  if (c.k == 8)
+    launch_combine_k<kBf16, 8>(c, blocks, stream);
+  else if (c.k == 4)
+    launch_combine_k<kBf16, 4>(c, blocks, stream);
   else
-    combine_kernel<kBf16, true><<<blocks, 256, 0, stream>>>(c);
+    launch_combine_k<kBf16, 0>(c, blocks, stream);
 }
 
 }  // namespace
