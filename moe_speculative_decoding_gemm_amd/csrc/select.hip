@@ -182,7 +182,8 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 // order), demand terms into sm.c[slot], anchor / natural-use flags, error
 // bits.  d, p, dp, cf: depth, parent, parent's depth and commit[depth] of
 // node i.
-template <int Q, int NPW>
+// KSM: K-slice partials loaded per logit (a bound on ksplit: 8 or kMaxKSplit)
+template <int Q, int NPW, int KSM>
 __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
                                            NodeSmem<NPW>& sm, int d, int p, int dp, float cf,
                                            const float* bias, const float* lrow) {
@@ -215,20 +216,20 @@ __device__ __forceinline__ void node_phase(const SelectArgs& a, int i, int slot,
     // for the front kernel of the DeepSeek-V3.1-shaped block).
     const size_t stride = static_cast<size_t>(a.N) * E;
     const int ksl = a.ksplit - 1;
-    float pv[Q][kMaxKSplit];
+    float pv[Q][KSM];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       valid[q] = e < E;
       const float* pp = a.part + static_cast<size_t>(i) * E + min(e, E - 1);
 #pragma unroll
-      for (int s = 0; s < kMaxKSplit; ++s) pv[q][s] = load_dev(pp + min(s, ksl) * stride);
+      for (int s = 0; s < KSM; ++s) pv[q][s] = load_dev(pp + min(s, ksl) * stride);
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       float sum = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxKSplit; ++s)
+      for (int s = 0; s < KSM; ++s)
         if (valid[q] && s < a.ksplit) sum += pv[q][s];
       l[q] = valid[q] ? sum + bias[q] : 0.f;
     }
@@ -901,7 +902,7 @@ __device__ __forceinline__ void router_partials(const SelectArgs& a, int g, int 
 // ------------------------------------------------------------- kernel ----
 // Q: 64-expert slots per lane, ceil(E / 64); NPW nodes per group (wave w of
 // NW takes nodes n0 + w, n0 + w + NW, ... in the node phase)
-template <typename AT, int Q, int NPW>
+template <typename AT, int Q, int NPW, int KSM>
 __global__ __launch_bounds__(64 * front_waves<NPW>()) void front_kernel(SelectArgs a) {
   constexpr int NW = front_waves<NPW>();
   constexpr int NTHR = 64 * NW;
@@ -969,7 +970,7 @@ __global__ __launch_bounds__(64 * front_waves<NPW>()) void front_kernel(SelectAr
   for (int s = 0; s < PER_WAVE; ++s) {
     const int slot = wave + NW * s;
     if (n0 + slot < N)
-      node_phase<Q, NPW>(a, n0 + slot, slot, sm, d[s], p[s], dp[s], cf[s], bias,
+      node_phase<Q, NPW, KSM>(a, n0 + slot, slot, sm, d[s], p[s], dp[s], cf[s], bias,
                          whole_k && !logits_in ? sm.lg[slot] : nullptr);
   }
   __syncthreads();
@@ -1213,14 +1214,25 @@ size_t fpart_bytes(int N, int E) { return static_cast<size_t>(fpart_stride(N, E)
 template <typename AT, int NPW>
 void launch_front(const SelectArgs& a, dim3 grid, int q, hipStream_t stream) {
   const int nthr = 64 * front_waves<NPW>();
-  if (q == 1)
-    front_kernel<AT, 1, NPW><<<grid, nthr, 0, stream>>>(a);
-  else if (q == 2)
-    front_kernel<AT, 2, NPW><<<grid, nthr, 0, stream>>>(a);
-  else if (q == 3)
-    front_kernel<AT, 3, NPW><<<grid, nthr, 0, stream>>>(a);
-  else
-    front_kernel<AT, 4, NPW><<<grid, nthr, 0, stream>>>(a);
+  if (a.ksplit <= 8) {
+    if (q == 1)
+      front_kernel<AT, 1, NPW, 8><<<grid, nthr, 0, stream>>>(a);
+    else if (q == 2)
+      front_kernel<AT, 2, NPW, 8><<<grid, nthr, 0, stream>>>(a);
+    else if (q == 3)
+      front_kernel<AT, 3, NPW, 8><<<grid, nthr, 0, stream>>>(a);
+    else
+      front_kernel<AT, 4, NPW, 8><<<grid, nthr, 0, stream>>>(a);
+  } else {
+    if (q == 1)
+      front_kernel<AT, 1, NPW, kMaxKSplit><<<grid, nthr, 0, stream>>>(a);
+    else if (q == 2)
+      front_kernel<AT, 2, NPW, kMaxKSplit><<<grid, nthr, 0, stream>>>(a);
+    else if (q == 3)
+      front_kernel<AT, 3, NPW, kMaxKSplit><<<grid, nthr, 0, stream>>>(a);
+    else
+      front_kernel<AT, 4, NPW, kMaxKSplit><<<grid, nthr, 0, stream>>>(a);
+  }
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
