@@ -157,6 +157,41 @@ def test_layer_parity_full(lib, name, tokens):
     assert np.max(np.abs(y_tok - ref["y"][tokens])) <= 1e-9 * np.max(np.abs(ref["y"]))
 
 
+@pytest.mark.timeout(900)
+def test_layer_parity_full_4096_natural(lib):
+    """The large-batch regime at its full size: the Qwen3-30B-shaped layer
+    under natural routing (standard speculative decoding) for 512 chains of
+    8 tokens, N = 4096 -- ~118 active experts with ~280 routed rows on
+    average and thousands for the most routed ones, so every active expert
+    runs in the GEMM kernels.  The whole y[4096, 2048] against the oracle's
+    grouped layer, the selection bit-exact given the GPU's logits."""
+    from workloads.gen import _CHAIN8_COMMIT
+    cfg = W.CONFIGS["qwen3_30b"].with_(tree="chains", commit=_CHAIN8_COMMIT, flags=1,
+                                       resident_slots=0, shared=False, N=4096,
+                                       n_chains=512, chain_len=8)
+    say("layer full 4096 natural: generating weights")
+    w = make_weights(cfg, device="cuda")
+    b = W.make_block(cfg, 0)
+    out, st = run_layer(lib, cfg, b, w)
+    lg = out["logits_out"].cpu().numpy()
+    sel = oracle_select(cfg, b, logits_in=lg)
+    assert check_selection(out, sel, st, cfg, "4096 natural")
+    assert (out["topk_idx"].cpu().numpy() == O.natural_topk(lg, cfg.k)).all()
+    active = O.permute(sel["topk_idx"], cfg.E)["active"]
+    rows = np.bincount(sel["topk_idx"].ravel(), minlength=cfg.E)
+    say(f"  U={st['n_active']}, most routed rows {rows.max()}: oracle layer")
+    assert rows.max() > 256  # the GEMM tiling's regime
+    ref = O.verify_block(
+        k=cfg.k, x=W.to_exact_f64(b.x), expert_fn=expert_fn_streaming(cfg, w, active),
+        parent=b.parent, depth=b.depth, commit=b.commit, logits_in=lg, resident=b.resident,
+        min_set=cfg.min_set, fixed_budget=cfg.fixed_budget, reroute_budget=cfg.reroute,
+        flags=cfg.flags)
+    assert (ref["topk_idx"] == sel["topk_idx"]).all()
+    err = max_rel_err(out["y"], ref["y"])
+    say(f"  whole-output rel err {err:.2e} (tol {TOL[cfg.w]})")
+    assert err <= TOL[cfg.w], err
+
+
 @pytest.mark.parametrize("pack", [False, True], ids=["rowmajor", "packed"])
 def test_separate_entry_points_match_verify_block(lib, pack):
     """acceptmoe_select -> moe_route_permute -> moe_grouped_swiglu (+ shared)
