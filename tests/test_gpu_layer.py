@@ -56,7 +56,7 @@ SMALL = [
     # more than 256 nodes: the restricted top-k runs as a kernel of its own
     ("qwen3_30b", dict(E=40, k=6, H=192, I=128, N=300)),
     # more work items than two per CU: the expert kernels cut items between
-    # work-groups (gate/up, then down; fp8 with NT = 2 and the shared expert)
+    # work-groups (gate/up, then down; fp8 with the shared expert)
     ("qwen3_30b", dict(E=40, k=8, H=192, I=2112, N=64)),
     ("qwen3_30b", dict(E=40, k=8, H=2112, I=192, N=64)),
     ("dsv31", dict(E=24, k=8, H=256, I=2304, N=64, n_chains=8, chain_len=8)),
